@@ -1,0 +1,42 @@
+"""The seeded input generators: reproducible and shaped as the workloads say."""
+import numpy as np
+import torch
+
+from block_diffusion_draft_ddtree_amd import synth
+
+
+def test_same_seed_same_bytes():
+    a = synth.drafter_logits(synth.TINY, 3)
+    b = synth.drafter_logits(synth.TINY, 3)
+    assert a.x.tobytes() == b.x.tobytes()
+    c = synth.drafter_logits(synth.TINY, 4)
+    assert a.x.tobytes() != c.x.tobytes()
+    q1 = synth.attention_inputs(synth.TINY)
+    q2 = synth.attention_inputs(synth.TINY)
+    assert q1.kv_bits.tobytes() == q2.kv_bits.tobytes()
+
+
+def test_bf16_rounding_matches_torch():
+    g = synth.rng("test", 50, 0)
+    x = (g.standard_normal(100000) * 10).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(bits, ref)
+    np.testing.assert_array_equal(synth.bf16_bits_to_f32(bits),
+                                  torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_peaked_generator_shape():
+    w = synth.QWEN3_8B
+    lg = synth.drafter_logits(w)
+    assert lg.x.shape == (16, 151936) and lg.x.dtype == np.float32
+    assert np.all(lg.peak != lg.runner)
+    i = np.arange(16)
+    # the boosted entries sit well above the N(0, 4) bulk
+    assert np.all(lg.x[i, lg.peak] > 2.0)
+
+
+def test_workload_table():
+    w = synth.CODER30B_B64
+    assert (w.N, w.G, w.mask_words, w.S_cap) == (65, 8, 3, 4096 + 65)
+    assert synth.sweep(512).mask_words == 17
