@@ -31,9 +31,12 @@ def test_peaked_generator_shape():
     lg = synth.drafter_logits(w)
     assert lg.x.shape == (16, 151936) and lg.x.dtype == np.float32
     assert np.all(lg.peak != lg.runner)
+    # Regenerating the unboosted bulk from the same stream isolates the boosts.
+    g = synth.rng(w.family, 0, synth.STREAM_LOGITS)
+    bulk = np.float32(2.0) * g.standard_normal((16, 151936), dtype=np.float32)
     i = np.arange(16)
-    # the boosted entries sit well above the N(0, 4) bulk
-    assert np.all(lg.x[i, lg.peak] > 2.0)
+    np.testing.assert_allclose(lg.x[i, lg.peak] - bulk[i, lg.peak], 9.0 - 0.4 * i, atol=1e-5)
+    np.testing.assert_allclose(lg.x[i, lg.runner] - bulk[i, lg.runner], 7.0 - 0.4 * i, atol=1e-5)
 
 
 def test_workload_table():
