@@ -1,0 +1,262 @@
+"""Benchmark of one DDTree verify round on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: ddtree_topk -> ddtree_build -> ddtree_tree_attn for
+every layer -> ddtree_accept_walk -> ddtree_kv_compact. Default workload:
+the Qwen3-Coder-30B-A3B verifier shape (32 q-heads / 4 kv-heads, head dim
+128, 48 layers, prefix 4096) with drafter logits [16, 151936] and budget
+B = 64. Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--graph]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="coder30b_b64")
+    ap.add_argument("--graph", action="store_true", help="replay the round as a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=30)
+    return ap.parse_args()
+
+
+def attn_work(w, depth: np.ndarray):
+    """Algorithmic bytes and flops of one ddtree_tree_attn launch."""
+    W = (w.N + 31) // 32
+    nbytes = (4 * w.Hkv * w.S * w.D          # prefix K and V, bf16
+              + 4 * w.Hkv * w.N * w.D        # tree-node K and V
+              + 4 * w.N * w.Hq * w.D         # Q in, O out
+              + 4 * w.N * W)                 # ancestor mask
+    flops = 4 * w.N * w.Hq * w.D * w.S + 4 * w.Hq * w.D * int((depth + 1).sum())
+    return nbytes, flops
+
+
+def topk_bytes(w):
+    return 4 * w.L * w.V + 8 * w.L * w.K
+
+
+def compact_bytes(w, a: int):
+    return 8 * a * w.layers * w.Hkv * w.D
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the hot path runs on a single MI355X "
+              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_diffusion_draft_ddtree_amd import binding as bd
+    from block_diffusion_draft_ddtree_amd import synth
+    from block_diffusion_draft_ddtree_amd.round import DraftTreeRound, RoundShape
+
+    bd.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    S_cap = w.S + w.N
+
+    # ---- inputs, resident in HBM -------------------------------------------
+    lg = synth.drafter_logits(w, 0)
+    logits = torch.from_numpy(lg.x).to(dev)
+    g = synth.rng(w.family, 0, synth.STREAM_QKV)
+    q = torch.empty((w.layers, w.N, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    kv = torch.empty((w.layers, 2, w.Hkv, S_cap, w.D), dtype=torch.bfloat16, device=dev)
+    for layer in range(w.layers):
+        qb, _ = synth.normal_bf16(g, (w.N, w.Hq, w.D))
+        q[layer].copy_(torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16))
+        kb, _ = synth.normal_bf16(g, (2, w.Hkv, S_cap, w.D))
+        kv[layer].copy_(torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16))
+    shape = RoundShape(w.L, w.V, w.K, w.B, w.Hq, w.Hkv, w.D, w.layers, S_cap)
+    rnd = DraftTreeRound(shape, w.S, dev)
+
+    # The target argmax per node follows the drafter's peak with p = 0.8 per
+    # depth; it depends on the tree's depths, so build the tree once first.
+    rnd.topk(logits)
+    rnd.build()
+    torch.cuda.synchronize()
+    depth = rnd.depth.cpu().numpy()
+    tgt_np = synth.target_argmax_follow_peak(depth, lg.peak, w.L, w.V,
+                                             synth.rng(w.family, 0, synth.STREAM_TARGET))
+    tgt = torch.from_numpy(tgt_np).to(dev)
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(attn_ev=None):
+        rnd.topk(logits)
+        rnd.build()
+        if attn_ev is not None:
+            attn_ev[0].record(stream)
+        for layer in range(w.layers):
+            rnd.attn(layer, q, kv, w.S)
+        if attn_ev is not None:
+            attn_ev[1].record(stream)
+        rnd.walk(tgt)
+        rnd.compact(kv, w.S)
+
+    graph = None
+    if args.graph:
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        graph.replay() if graph is not None else step()
+    torch.cuda.synchronize()
+
+    # ---- timed region -------------------------------------------------------
+    attn_pairs = [(ev(), ev()) for _ in range(args.steps)]
+    e0, e1 = ev(), ev()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step(attn_pairs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_us = (t1 - t0) * 1e6 / args.steps
+    gpu_us = e0.elapsed_time(e1) * 1e3 / args.steps
+
+    # ---- per-stage device time (HIP events on the launch stream) ----------
+    R = args.stage_reps
+
+    def timed(fn, reps):
+        a, b = ev(), ev()
+        fn()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    stage = {}
+    stage["topk"] = timed(lambda i=0: rnd.topk(logits), R)
+    stage["build"] = timed(lambda i=0: rnd.build(), R)
+    stage["tree_attn"] = timed(lambda i=0: rnd.attn(i % w.layers, q, kv, w.S), max(R, 2 * w.layers))
+    stage["walk"] = timed(lambda i=0: rnd.walk(tgt), R)
+    stage["kv_compact"] = timed(lambda i=0: rnd.compact(kv, w.S), R)
+    if graph is None:
+        attn_live = [a.elapsed_time(b) * 1e3 / w.layers for a, b in attn_pairs]
+        attn_us = float(np.mean(attn_live))
+    else:
+        attn_us = stage["tree_attn"]
+    torch.cuda.synchronize()
+    a_acc = int(rnd.n_acc.cpu()[0])
+    depth = rnd.depth.cpu().numpy()
+
+    nbytes, flops = attn_work(w, depth)
+    hbm_gbs = nbytes / (attn_us * 1e-6) / 1e9
+    tflops = flops / (attn_us * 1e-6) / 1e12
+    bound = "mfma" if flops / nbytes > MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "ddtree_tree_attn"
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = flops
+
+    value = gpu_us
+    result = {
+        "metric": "tree-verify attn µs & HBM TB/s at B=64, ctx 4k; full round µs/step",
+        "value": round(value, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(value / 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy generators; no weights or datasets)",
+        "config": {"workload": w.name, "L": w.L, "V": w.V, "K": w.K, "B": w.B, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "D": w.D, "S": w.S, "layers": w.layers,
+                   "mode": "hip-graph" if graph is not None else "eager"},
+        "tree_attn_us": round(attn_us, 3),
+        "tree_attn_TBps": round(hbm_gbs / 1e3, 3),
+        "tree_attn_hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "tree_attn_mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4),
+        "round_wall_us": round(wall_us, 2),
+        "stage_us": {k: round(v, 3) for k, v in stage.items()},
+        "topk_TBps": round(topk_bytes(w) / (stage["topk"] * 1e-6) / 1e12, 3),
+        "accepted": a_acc,
+        "depth_hist": np.bincount(depth).tolist(),
+        "roofline": roof,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, lg, depth, tgt_np)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, lg, depth, tgt_np):
+    """The CPU oracle on a bounded sample of one round, scaled to a round."""
+    from threadpoolctl import threadpool_info
+
+    from block_diffusion_draft_ddtree_amd import synth
+    from oracle import attention as oa
+    from oracle import commit as oc
+    from oracle import softmax_topk as st
+    from oracle import tree as ot
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    t = {}
+    t0 = time.perf_counter()
+    lp, tok = st.topk(lg.x, w.K)
+    t["topk"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    tree = ot.build_tree(lp.astype(np.float32), tok, w.B, 0)
+    t["build"] = time.perf_counter() - t0
+    qkv = synth.attention_inputs(w, layers=1)
+    t0 = time.perf_counter()
+    oa.tree_attention(qkv.q, qkv.kv[0, 0], qkv.kv[0, 1], w.S, tree.anc)
+    t["attn_layer"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    acc, a, _ = oc.accept_walk(tree.parent, tree.token, tgt_np, w.L)
+    t["walk"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oc.kv_compact(qkv.kv_bits[0], w.S, acc, a)
+    t["compact_layer"] = time.perf_counter() - t0
+    us = 1e6 * (t["topk"] + t["build"] + w.layers * t["attn_layer"] + t["walk"]
+                + w.layers * t["compact_layer"])
+    return {"value": round(us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": (f"one round of {w.name}: top-K over all {w.L} rows, tree build, "
+                       f"attention and compaction of 1 of {w.layers} layers (each scaled "
+                       f"x{w.layers}), walk"),
+            "stage_s": {k: round(v, 4) for k, v in t.items()}}
+
+
+if __name__ == "__main__":
+    main()

@@ -13,6 +13,6 @@ __all__ = ["synth", "binding"]
 
 def __getattr__(name):
     if name == "binding":
-        from . import binding
-        return binding
+        import importlib
+        return importlib.import_module(__name__ + ".binding")
     raise AttributeError(name)

@@ -1,0 +1,207 @@
+"""ctypes binding of libddtree (same names as the C ABI in include/ddtree.h).
+
+Argument marshalling only: torch device tensors become raw device pointers
+and the current torch stream becomes the HIP stream; every step of the path
+runs in the library's HIP kernels. Outputs and workspaces that are not
+passed in are allocated with torch (device memory plumbing). A missing
+library is an error: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libddtree.so")
+
+DDTREE_OK = 0
+DDTREE_ERR_INVALID_ARGUMENT = 1
+DDTREE_ERR_UNSUPPORTED = 2
+DDTREE_ERR_WORKSPACE_TOO_SMALL = 3
+DDTREE_ERR_HIP = 4
+
+MAX_L, MAX_K, MAX_B, MAX_LK = 32, 1024, 1024, 32768
+
+_lib = None
+_vp, _i32, _i64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                              ctypes.c_float, ctypes.c_size_t)
+
+_SIGNATURES = {
+    "ddtree_status_string": (ctypes.c_char_p, [_i32]),
+    "ddtree_version": (_i32, []),
+    "ddtree_topk_workspace_bytes": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "ddtree_topk": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "ddtree_build": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
+    "ddtree_tree_attn_workspace_bytes": (_i32, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "ddtree_tree_attn": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
+                                _i32, _vp, _vp, _sz, _vp]),
+    "ddtree_accept_walk": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "ddtree_kv_compact": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+}
+EXPORTS = tuple(_SIGNATURES)
+
+
+class DDTreeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {ddtree_status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libddtree.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing; build it with "
+                "`python -m block_diffusion_draft_ddtree_amd.build_lib`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != DDTREE_OK:
+        raise DDTreeError(status, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def ddtree_status_string(status: int) -> str:
+    return lib().ddtree_status_string(int(status)).decode()
+
+
+def ddtree_version() -> int:
+    return lib().ddtree_version()
+
+
+def ddtree_topk_workspace_bytes(L: int, V: int, K: int) -> int:
+    out = _sz(0)
+    _check(lib().ddtree_topk_workspace_bytes(L, V, K, ctypes.byref(out)), "ddtree_topk_workspace_bytes")
+    return out.value
+
+
+def ddtree_tree_attn_workspace_bytes(N: int, Hq: int, Hkv: int, D: int, S: int) -> int:
+    out = _sz(0)
+    _check(lib().ddtree_tree_attn_workspace_bytes(N, Hq, Hkv, D, S, ctypes.byref(out)),
+           "ddtree_tree_attn_workspace_bytes")
+    return out.value
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def ddtree_topk(logits: torch.Tensor, K: int, logp=None, token=None, ws=None, stream=None):
+    """fp32 logits [L, V] (row stride may exceed V) -> (logp fp32 [L, K], token int32 [L, K])."""
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [L, V] with unit column stride")
+    L, V = logits.shape
+    if logits.dtype != torch.float32 or not logits.is_cuda:
+        raise ValueError("logits must be a float32 device tensor")
+    dev = logits.device
+    logp = torch.empty((L, K), dtype=torch.float32, device=dev) if logp is None else logp
+    token = torch.empty((L, K), dtype=torch.int32, device=dev) if token is None else token
+    need = ddtree_topk_workspace_bytes(L, V, K)
+    ws = workspace(need, dev) if ws is None else ws
+    _check(lib().ddtree_topk(logits.data_ptr(), logits.stride(0), L, V, K,
+                             _dev(logp, torch.float32, "logp"), _dev(token, torch.int32, "token"),
+                             _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "ddtree_topk")
+    return logp, token
+
+
+def ddtree_build(logp: torch.Tensor, token: torch.Tensor, B: int, root_token: torch.Tensor,
+                 mask_words: int | None = None, parent=None, depth=None, node_token=None,
+                 score=None, anc=None, want_score: bool = True, stream=None):
+    """[L, K] tables -> (parent, depth, node_token, score, anc) for N = B + 1 nodes."""
+    L, K = logp.shape
+    N = B + 1
+    W = (N + 31) // 32 if mask_words is None else mask_words
+    dev = logp.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    parent = torch.empty(N, **i32) if parent is None else parent
+    depth = torch.empty(N, **i32) if depth is None else depth
+    node_token = torch.empty(N, **i32) if node_token is None else node_token
+    if score is None and want_score:
+        score = torch.empty(N, dtype=torch.float32, device=dev)
+    anc = torch.empty((N, W), **i32) if anc is None else anc
+    _check(lib().ddtree_build(
+        _dev(logp, torch.float32, "logp"), _dev(token, torch.int32, "token"), L, K, B,
+        _dev(root_token, torch.int32, "root_token"), _dev(parent, torch.int32, "parent"),
+        _dev(depth, torch.int32, "depth"), _dev(node_token, torch.int32, "node_token"),
+        None if score is None else _dev(score, torch.float32, "score"),
+        _dev(anc, anc.dtype, "anc"), W, _stream(stream)), "ddtree_build")
+    return parent, depth, node_token, score, anc
+
+
+def ddtree_tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: int,
+                     anc: torch.Tensor, scale: float | None = None, out=None, ws=None,
+                     stream=None) -> torch.Tensor:
+    """q bf16 [N, Hq, D]; k, v bf16 [Hkv, S_cap, D]; anc [N, W] -> out bf16 [N, Hq, D]."""
+    N, Hq, D = q.shape
+    Hkv, S_cap, Dk = k.shape
+    if Dk != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [Hkv, S_cap, D] with q's D")
+    if anc.dim() != 2 or anc.shape[0] < N:
+        raise ValueError("anc must be [N, mask_words]")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    need = ddtree_tree_attn_workspace_bytes(N, Hq, Hkv, D, S)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check(lib().ddtree_tree_attn(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        S, S_cap, N, Hq, Hkv, D, scale, _dev(anc, anc.dtype, "anc"), anc.shape[1],
+        _dev(out, torch.bfloat16, "out"), _dev(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream)), "ddtree_tree_attn")
+    return out
+
+
+def ddtree_accept_walk(parent: torch.Tensor, node_token: torch.Tensor, L: int,
+                       target_argmax: torch.Tensor, acc=None, n_acc=None, next_bonus=None,
+                       stream=None):
+    """-> (acc int32 [L + 1], n_acc int32 [1], next_bonus int32 [1]) on the device."""
+    N = parent.shape[0]
+    dev = parent.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    acc = torch.empty(L + 1, **i32) if acc is None else acc
+    n_acc = torch.empty(1, **i32) if n_acc is None else n_acc
+    next_bonus = torch.empty(1, **i32) if next_bonus is None else next_bonus
+    _check(lib().ddtree_accept_walk(
+        _dev(parent, torch.int32, "parent"), _dev(node_token, torch.int32, "node_token"), N, L,
+        _dev(target_argmax, torch.int32, "target_argmax"), _dev(acc, torch.int32, "acc"),
+        _dev(n_acc, torch.int32, "n_acc"), _dev(next_bonus, torch.int32, "next_bonus"),
+        _stream(stream)), "ddtree_accept_walk")
+    return acc, n_acc, next_bonus
+
+
+def ddtree_kv_compact(kv: torch.Tensor, S: int, N: int, L: int, acc: torch.Tensor,
+                      n_acc: torch.Tensor, stream=None) -> None:
+    """In place on kv bf16 [layers, 2, Hkv, S_cap, D]."""
+    layers, two, Hkv, S_cap, D = kv.shape
+    if two != 2:
+        raise ValueError("kv must be [layers, 2, Hkv, S_cap, D]")
+    _check(lib().ddtree_kv_compact(
+        _dev(kv, torch.bfloat16, "kv"), layers, Hkv, S_cap, D, S, N, L,
+        _dev(acc, torch.int32, "acc"), _dev(n_acc, torch.int32, "n_acc"), _stream(stream)),
+        "ddtree_kv_compact")

@@ -1,0 +1,141 @@
+// C ABI of libddtree: argument validation on the host, then kernel launches.
+// Declarations and semantics: include/ddtree.h.
+#include <cstdint>
+
+#include "common.hpp"
+
+#define DDT_API extern "C" __attribute__((visibility("default")))
+
+namespace ddt_host {
+
+int launch_status(hipError_t e) { return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP; }
+
+}  // namespace ddt_host
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// sum_{d=1..L} K^d >= B, without overflow.
+bool enough_prefixes(int L, int K, int B) {
+  int64_t total = 0, pw = 1;
+  for (int d = 1; d <= L; ++d) {
+    pw *= K;
+    total += pw;
+    if (total >= B) return true;
+  }
+  return total >= B;
+}
+
+int topk_check(int L, int V, int K) {
+  if (L < 1 || V < 1 || K < 1) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (K > V) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (L > DDTREE_MAX_L || K > DDTREE_MAX_K) return DDTREE_ERR_UNSUPPORTED;
+  return DDTREE_OK;
+}
+
+int attn_check(int N, int Hq, int Hkv, int D, int S) {
+  if (N < 1 || Hq < 1 || Hkv < 1 || S < 0) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (Hq % Hkv != 0) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (N > DDTREE_MAX_B + 1) return DDTREE_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return DDTREE_ERR_UNSUPPORTED;
+  if ((int64_t)N * Hq > (int64_t)1 << 30) return DDTREE_ERR_UNSUPPORTED;
+  return DDTREE_OK;
+}
+
+}  // namespace
+
+DDT_API const char* ddtree_status_string(int status) {
+  switch (status) {
+    case DDTREE_OK: return "DDTREE_OK";
+    case DDTREE_ERR_INVALID_ARGUMENT: return "DDTREE_ERR_INVALID_ARGUMENT";
+    case DDTREE_ERR_UNSUPPORTED: return "DDTREE_ERR_UNSUPPORTED";
+    case DDTREE_ERR_WORKSPACE_TOO_SMALL: return "DDTREE_ERR_WORKSPACE_TOO_SMALL";
+    case DDTREE_ERR_HIP: return "DDTREE_ERR_HIP";
+    default: return "DDTREE_ERR_UNKNOWN";
+  }
+}
+
+DDT_API int ddtree_version(void) { return 100; }
+
+DDT_API int ddtree_topk_workspace_bytes(int L, int V, int K, size_t* bytes) {
+  if (!bytes) return DDTREE_ERR_INVALID_ARGUMENT;
+  const int st = topk_check(L, V, K);
+  if (st) return st;
+  *bytes = ddt_host::topk_plan(L, V, K).bytes;
+  return DDTREE_OK;
+}
+
+DDT_API int ddtree_topk(const float* logits, int64_t row_stride, int L, int V, int K, float* logp,
+                        int32_t* token, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int st = topk_check(L, V, K);
+  if (st) return st;
+  if (!logits || !logp || !token || !ws) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (row_stride < V) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < ddt_host::topk_plan(L, V, K).bytes) return DDTREE_ERR_WORKSPACE_TOO_SMALL;
+  return ddt_host::topk_launch(logits, row_stride, L, V, K, logp, token, ws, stream);
+}
+
+DDT_API int ddtree_build(const float* logp, const int32_t* token, int L, int K, int B,
+                         const int32_t* root_token, int32_t* parent, int32_t* depth,
+                         int32_t* node_token, float* score, uint32_t* anc, int mask_words,
+                         hipStream_t stream) {
+  if (L < 1 || K < 1 || B < 1) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (L > DDTREE_MAX_L || K > DDTREE_MAX_K || B > DDTREE_MAX_B) return DDTREE_ERR_UNSUPPORTED;
+  if ((int64_t)L * K > DDTREE_MAX_LK) return DDTREE_ERR_UNSUPPORTED;
+  if (!enough_prefixes(L, K, B)) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (!logp || !token || !root_token || !parent || !depth || !node_token || !anc)
+    return DDTREE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)mask_words * 32 < B + 1) return DDTREE_ERR_INVALID_ARGUMENT;
+  return ddt_host::build_launch(logp, token, L, K, B, root_token, parent, depth, node_token, score,
+                                anc, mask_words, stream);
+}
+
+DDT_API int ddtree_tree_attn_workspace_bytes(int N, int Hq, int Hkv, int D, int S, size_t* bytes) {
+  if (!bytes) return DDTREE_ERR_INVALID_ARGUMENT;
+  const int st = attn_check(N, Hq, Hkv, D, S);
+  if (st) return st;
+  *bytes = ddt_host::attn_plan(N, Hq, Hkv, D, S).bytes;
+  return DDTREE_OK;
+}
+
+DDT_API int ddtree_tree_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int S,
+                             int S_cap, int N, int Hq, int Hkv, int D, float scale,
+                             const uint32_t* anc, int mask_words, uint16_t* out, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  const int st = attn_check(N, Hq, Hkv, D, S);
+  if (st) return st;
+  if (!q || !k || !v || !anc || !out) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return DDTREE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)S + N > S_cap) return DDTREE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)mask_words * 32 < N) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f) || scale != scale || scale > 3.0e38f) return DDTREE_ERR_INVALID_ARGUMENT;
+  const size_t need = ddt_host::attn_plan(N, Hq, Hkv, D, S).bytes;
+  if (need && (!ws || ws_bytes < need)) return DDTREE_ERR_WORKSPACE_TOO_SMALL;
+  return ddt_host::attn_launch(q, k, v, S, S_cap, N, Hq, Hkv, D, scale, anc, mask_words, out, ws,
+                               stream);
+}
+
+DDT_API int ddtree_accept_walk(const int32_t* parent, const int32_t* node_token, int N, int L,
+                               const int32_t* target_argmax, int32_t* acc, int32_t* n_acc,
+                               int32_t* next_bonus, hipStream_t stream) {
+  if (N < 1 || L < 1) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (L > DDTREE_MAX_L || N > DDTREE_MAX_B + 1) return DDTREE_ERR_UNSUPPORTED;
+  if (!parent || !node_token || !target_argmax || !acc || !n_acc || !next_bonus)
+    return DDTREE_ERR_INVALID_ARGUMENT;
+  return ddt_host::walk_launch(parent, node_token, N, L, target_argmax, acc, n_acc, next_bonus,
+                               stream);
+}
+
+DDT_API int ddtree_kv_compact(uint16_t* kv, int layers, int Hkv, int S_cap, int D, int S, int N,
+                              int L, const int32_t* acc, const int32_t* n_acc,
+                              hipStream_t stream) {
+  if (layers < 1 || Hkv < 1 || S < 0 || N < 1 || L < 1) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (L > DDTREE_MAX_L) return DDTREE_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return DDTREE_ERR_UNSUPPORTED;
+  if (!kv || !acc || !n_acc || !aligned16(kv)) return DDTREE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)S + N > S_cap) return DDTREE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)layers * 2 * Hkv > 0x7FFFFFFF) return DDTREE_ERR_UNSUPPORTED;
+  return ddt_host::compact_launch(kv, layers, Hkv, S_cap, D, S, acc, n_acc, stream);
+}

@@ -1,0 +1,40 @@
+// Host-side launchers of libddtree's kernels (internal; one per .hip file).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ddt_host {
+
+int launch_status(hipError_t e);
+
+// ddtree_topk: chunk kernel + merge kernel; workspace carve-up.
+struct TopkPlan {
+  int C, cap, idx_passes;
+  size_t stats_off, counts_off, candx_off, candi_off, bytes;
+};
+TopkPlan topk_plan(int L, int V, int K);
+int topk_launch(const float* logits, int64_t stride, int L, int V, int K, float* logp,
+                int32_t* token, void* ws, hipStream_t stream);
+
+int build_launch(const float* logp, const int32_t* token, int L, int K, int B,
+                 const int32_t* root_token, int32_t* parent, int32_t* depth,
+                 int32_t* node_token, float* score, uint32_t* anc, int W, hipStream_t stream);
+
+// ddtree_tree_attn: grid shape and split-partial workspace.
+struct AttnPlan {
+  int tiles, splits, blocks_per_split, rows_pad;
+  size_t part_o_off, part_ml_off, bytes;
+};
+AttnPlan attn_plan(int N, int Hq, int Hkv, int D, int S);
+int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int S, int S_cap, int N,
+                int Hq, int Hkv, int D, float scale, const uint32_t* anc, int W, uint16_t* out,
+                void* ws, hipStream_t stream);
+
+int walk_launch(const int32_t* parent, const int32_t* tok, int N, int L, const int32_t* tgt,
+                int32_t* acc, int32_t* n_acc, int32_t* bonus, hipStream_t stream);
+int compact_launch(uint16_t* kv, int layers, int Hkv, int S_cap, int D, int S,
+                   const int32_t* acc, const int32_t* n_acc, hipStream_t stream);
+
+}  // namespace ddt_host

@@ -1,0 +1,86 @@
+"""One DDTree decode round on the device: topk -> build -> tree attention per
+layer -> accept walk -> KV compaction ("DDTree Deep Dive", section 3: the
+draft, tree_build, tree_compile, verify, commit stages; the drafter forward
+and the target's non-attention layers are outside this library).
+
+All buffers are allocated once (torch device memory) so a round enqueues
+only libddtree kernels, which also makes the round capturable in a HIP
+graph. The next round's root token is the walk's ``next_bonus`` buffer.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import binding as bd
+
+
+@dataclass
+class RoundShape:
+    L: int
+    V: int
+    K: int
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    layers: int
+    S_cap: int
+
+    @property
+    def N(self) -> int:
+        return self.B + 1
+
+    @property
+    def W(self) -> int:
+        return (self.N + 31) // 32
+
+
+class DraftTreeRound:
+    def __init__(self, shape: RoundShape, S_max: int, device="cuda"):
+        s = shape
+        self.shape = s
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.logp = torch.empty((s.L, s.K), dtype=torch.float32, device=dev)
+        self.token = torch.empty((s.L, s.K), **i32)
+        self.ws_topk = bd.workspace(bd.ddtree_topk_workspace_bytes(s.L, s.V, s.K), dev)
+        self.root_token = torch.zeros(1, **i32)
+        self.parent = torch.empty(s.N, **i32)
+        self.depth = torch.empty(s.N, **i32)
+        self.node_token = torch.empty(s.N, **i32)
+        self.score = torch.empty(s.N, dtype=torch.float32, device=dev)
+        self.anc = torch.empty((s.N, s.W), **i32)
+        self.attn_out = torch.empty((s.layers, s.N, s.Hq, s.D), dtype=torch.bfloat16, device=dev)
+        self.ws_attn = bd.workspace(bd.ddtree_tree_attn_workspace_bytes(s.N, s.Hq, s.Hkv, s.D, S_max), dev)
+        self.acc = torch.empty(s.L + 1, **i32)
+        self.n_acc = torch.empty(1, **i32)
+        self.next_bonus = torch.empty(1, **i32)
+
+    def topk(self, logits):
+        bd.ddtree_topk(logits, self.shape.K, self.logp, self.token, self.ws_topk)
+
+    def build(self):
+        bd.ddtree_build(self.logp, self.token, self.shape.B, self.root_token, self.shape.W,
+                        self.parent, self.depth, self.node_token, self.score, self.anc)
+
+    def attn(self, layer: int, q, kv, S: int):
+        bd.ddtree_tree_attn(q[layer], kv[layer, 0], kv[layer, 1], S, self.anc,
+                            out=self.attn_out[layer], ws=self.ws_attn)
+
+    def walk(self, target_argmax):
+        bd.ddtree_accept_walk(self.parent, self.node_token, self.shape.L, target_argmax,
+                              self.acc, self.n_acc, self.next_bonus)
+
+    def compact(self, kv, S: int):
+        bd.ddtree_kv_compact(kv, S, self.shape.N, self.shape.L, self.acc, self.n_acc)
+
+    def run(self, logits, q, kv, S: int, target_argmax):
+        """Enqueue one full round on the current stream (no host sync)."""
+        self.topk(logits)
+        self.build()
+        for layer in range(self.shape.layers):
+            self.attn(layer, q, kv, S)
+        self.walk(target_argmax)
+        self.compact(kv, S)

@@ -1,0 +1,204 @@
+/*
+ * libddtree -- DDTree's per-round draft-tree hot path on AMD MI355X (gfx950).
+ *
+ * One decode round of block-diffusion speculative decoding with draft trees:
+ *
+ *   ddtree_topk         log-softmax + top-K of the drafter's per-position logits
+ *   ddtree_build        best-first top-B prefix tree, node arrays, ancestor mask
+ *   ddtree_tree_attn    ancestor-only GQA attention of the tree nodes (per layer)
+ *   ddtree_accept_walk  greedy walk of the target's argmax down the tree
+ *   ddtree_kv_compact   in-place gather of the accepted path's K/V rows
+ *
+ * Sources (the web pages on DDTree; cited by page title and section):
+ *   [DD]  "DDTree Deep Dive: Algorithm, Code, and Engineering Philosophy of
+ *         Block Diffusion Draft Trees" (zhichai.net forum topic).
+ *   [AH]  "DDTree: Turning Block Diffusion Drafters into Tree-Based Speculative
+ *         Decoders" (alanhou.org blog summary).
+ *   [AB]  "Qwen3-Coder-30B-A3B - DDTree vs DFlash vs autoregressive -
+ *         single-stream (batch-1)" (autobench config page).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer is a DEVICE pointer unless its comment says "host".
+ * - bf16 tensors are passed as uint16_t bit patterns (IEEE bfloat16).
+ * - All arrays are dense row-major with the shapes given; the caller owns
+ *   every buffer. The library allocates nothing, keeps no pointer after a
+ *   call returns and holds no mutable global state: calls are re-entrant and
+ *   thread-safe.
+ * - Every call validates its arguments on the host first; on error it
+ *   returns a non-zero ddtree_status and enqueues nothing. On success the
+ *   work is enqueued on `stream` (may be 0 = null stream) and the call
+ *   returns without synchronising; outputs are valid once the stream has
+ *   reached that point. Kernel launch failures return DDTREE_ERR_HIP.
+ * - Device-resident inputs (token ids, parents, counts) are trusted: they
+ *   must satisfy the documented ranges; the host cannot check them.
+ * - Vector loads need 16-byte aligned q/k/v/out pointers (checked).
+ */
+#ifndef DDTREE_H
+#define DDTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ddtree_status {
+  DDTREE_OK = 0,
+  DDTREE_ERR_INVALID_ARGUMENT = 1,   /* a size, pointer or alignment is wrong */
+  DDTREE_ERR_UNSUPPORTED = 2,        /* valid but outside what the kernels do */
+  DDTREE_ERR_WORKSPACE_TOO_SMALL = 3,/* ws_bytes below the queried size        */
+  DDTREE_ERR_HIP = 4                 /* a HIP launch or runtime call failed    */
+} ddtree_status;
+
+/* Limits checked by the calls below. */
+#define DDTREE_MAX_L 32        /* drafted block positions (the pages use 16) */
+#define DDTREE_MAX_K 1024      /* top-K kept per position                    */
+#define DDTREE_MAX_B 1024      /* node budget (the pages sweep 16..1024)     */
+#define DDTREE_MAX_LK 32768    /* L * K: the whole top-K table sits in LDS   */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* ddtree_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int ddtree_version(void);
+
+/* ------------------------------------------------------------------------
+ * ddtree_topk -- fused log-softmax and top-K per drafted block position.
+ *
+ * Source: [DD] section 1 (one drafter pass gives a marginal q_i per block
+ * position), section 2 Lemma 1 (only the top K = min(B, |V|) tokens of each
+ * position matter); [AH] Key Concepts (node scores are sums of log-probs).
+ *
+ * logits      fp32 [L, row_stride]; row i holds V logits of block position i
+ *             (0-based). Values must be finite.
+ * row_stride  elements between rows, >= V.
+ * L, V, K     1 <= L <= DDTREE_MAX_L, 1 <= K <= min(V, DDTREE_MAX_K).
+ * logp        out fp32 [L, K]: log q_i of the selected tokens, rank order.
+ * token       out int32 [L, K]: their token ids.
+ * ws/ws_bytes device scratch of at least ddtree_topk_workspace_bytes().
+ *
+ * Ranking is by logit, larger first; exact ties go to the smaller token id
+ * (+0 and -0 are equal). logp = x - lse_i with lse_i = log sum_v exp x[i,v]
+ * computed in fp32 (max-subtracted); |error| <= 1e-5 against fp64.
+ * ---------------------------------------------------------------------- */
+int ddtree_topk_workspace_bytes(int L, int V, int K, size_t* bytes /* host */);
+int ddtree_topk(const float* logits, int64_t row_stride, int L, int V, int K,
+                float* logp, int32_t* token, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * ddtree_build -- best-first selection of the top-B prefixes and the tree.
+ *
+ * Source: [DD] section 2, Proposition 3 (max-heap over rank tuples; each pop
+ * pushes the next sibling and the first child; pops exactly the top-B
+ * prefixes, which by Proposition 2 form a prefix-closed optimal tree);
+ * section 3 (tree encoded as position/parent pairs); section 4 and [AH] Key
+ * Concepts (each node sees the root, its ancestors and itself).
+ *
+ * logp, token  fp32 / int32 [L, K], each row non-increasing in logp (the
+ *              output of ddtree_topk); logp <= 0.
+ * B            node budget, 1 <= B <= min(DDTREE_MAX_B, sum_{d=1..L} K^d);
+ *              the tree has N = B + 1 nodes.
+ * root_token   int32 device scalar: the round's bonus token (node 0).
+ * parent       out int32 [N]: parent node, -1 for the root; parent[n] < n.
+ * depth        out int32 [N]: 0 for the root, else 1..L.
+ * node_token   out int32 [N]: node 0 = *root_token; node n at depth d with
+ *              last rank r has token[(d-1)*K + r].
+ * score        out fp32 [N] or NULL: 0 for the root, else the fp32
+ *              left-to-right sum of logp along the rank tuple.
+ * anc          out uint32 [N, mask_words]: bit j of row n (word j>>5, bit
+ *              j&31) is set iff node j is n or an ancestor of n; other bits 0.
+ * mask_words   >= ceil(N / 32).
+ *
+ * Nodes 1..B are the selected prefixes in pop order: higher score first;
+ * equal scores by lexicographically smaller rank tuple (a proper prefix is
+ * smaller). The result is unique and bit-exact. Runs as one workgroup.
+ * ---------------------------------------------------------------------- */
+int ddtree_build(const float* logp, const int32_t* token, int L, int K, int B,
+                 const int32_t* root_token, int32_t* parent, int32_t* depth,
+                 int32_t* node_token, float* score, uint32_t* anc,
+                 int mask_words, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * ddtree_tree_attn -- ancestor-only tree attention of one layer (GQA, bf16).
+ *
+ * Source: [DD] section 4 (a node attends to the cached past context, the
+ * root, its ancestors and itself, never to other branches), section 10
+ * (the verifier attention is Qwen3's grouped-query attention); [AH] Core
+ * Mechanism (all nodes are verified in one target forward pass); [AB] (the
+ * ancestor mask is why the verifier cannot use a plain causal kernel).
+ *
+ * q        bf16 [N, Hq, D]: node n's query for head h (RoPE already applied).
+ * k, v     bf16 [Hkv, S_cap, D] each: rows [0, S) are the cached prefix,
+ *          row S + m holds tree node m (m < N).
+ * S        prefix length, >= 0; S + N <= S_cap.
+ * N        tree nodes incl. the root, 1 <= N <= DDTREE_MAX_B + 1.
+ * Hq, Hkv  Hq % Hkv == 0; query head h reads kv-head h / (Hq / Hkv).
+ * D        64 or 128.
+ * scale    softmax scale (typically 1/sqrt(D)).
+ * anc      uint32 [N, mask_words] as produced by ddtree_build.
+ * out      out bf16 [N, Hq, D]; must not alias q, k or v.
+ * ws       scratch of at least ddtree_tree_attn_workspace_bytes().
+ *
+ * out[n,h] = sum_j softmax_j(scale * q[n,h] . k[g,j]) v[g,j] over rows
+ * j in [0,S) and j = S + m for every m set in anc[n]; fp32 accumulation and
+ * online softmax, bf16 rounding of the softmax weights before the P.V
+ * product; output rounded to bf16 (to nearest even).
+ * ---------------------------------------------------------------------- */
+int ddtree_tree_attn_workspace_bytes(int N, int Hq, int Hkv, int D, int S,
+                                     size_t* bytes /* host */);
+int ddtree_tree_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     int S, int S_cap, int N, int Hq, int Hkv, int D,
+                     float scale, const uint32_t* anc, int mask_words,
+                     uint16_t* out, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * ddtree_accept_walk -- greedy verification walk down the tree.
+ *
+ * Source: [DD] section 6 (walk state machine: follow the child whose token
+ * matches the target's choice; the first unmatched target token becomes the
+ * next bonus token); [AH] Core Mechanism (the longest matching path is
+ * accepted).
+ *
+ * parent, node_token  int32 [N] from ddtree_build (parent[n] < n; sibling
+ *                     tokens distinct).
+ * target_argmax       int32 [N]: the target's greedy token after node n.
+ * L                   tree depth bound (1..DDTREE_MAX_L).
+ * acc                 out int32 [L + 1]: acc[0] = 0 (root), acc[1..a] the
+ *                     accepted nodes root-to-leaf, acc[a+1..L] = -1.
+ * n_acc               out int32 device scalar: a = accepted drafted tokens.
+ * next_bonus          out int32 device scalar: target_argmax[acc[a]]; may be
+ *                     passed as the next round's root_token.
+ * ---------------------------------------------------------------------- */
+int ddtree_accept_walk(const int32_t* parent, const int32_t* node_token, int N,
+                       int L, const int32_t* target_argmax, int32_t* acc,
+                       int32_t* n_acc, int32_t* next_bonus, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * ddtree_kv_compact -- keep only the accepted path in the KV cache, in place.
+ *
+ * Source: [DD] section 5 (tree tokens are interleaved in the cache tail, so
+ * the accepted rows are gathered in place; without it the cache grows by
+ * the budget every round); [AB] (the in-place tail compaction is the
+ * method's fair path).
+ *
+ * kv       bf16 [layers, 2, Hkv, S_cap, D]: every layer's K then V half.
+ * S        prefix length of this round; rows S..S+N-1 hold the tree.
+ * acc      int32 [L + 1] and n_acc (device scalar, 0..L) from the walk.
+ *
+ * For every layer, half and kv-head: row S + k <- row S + acc[k] for
+ * k = 1..a (all reads happen before any write of a slice). Rows below S + 1
+ * and from S + 1 + a on are untouched. The new cache length is S + 1 + a.
+ * ---------------------------------------------------------------------- */
+int ddtree_kv_compact(uint16_t* kv, int layers, int Hkv, int S_cap, int D,
+                      int S, int N, int L, const int32_t* acc,
+                      const int32_t* n_acc, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DDTREE_H */

@@ -1,0 +1,111 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/ddtree.h declares, and rejects invalid arguments on the host with
+the documented status codes before any HIP call (null pointers are passed
+where a device buffer would go; validation never dereferences them)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_draft_ddtree_amd import binding as bd
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ddtree.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return bd.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddtree_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(bd.EXPORTS)
+
+
+def test_status_strings_and_version(lib):
+    assert bd.ddtree_status_string(0) == "DDTREE_OK"
+    assert bd.ddtree_status_string(3) == "DDTREE_ERR_WORKSPACE_TOO_SMALL"
+    assert bd.ddtree_status_string(99) == "DDTREE_ERR_UNKNOWN"
+    assert bd.ddtree_version() >= 100
+
+
+def test_workspace_queries(lib):
+    ws = bd.ddtree_topk_workspace_bytes(16, 151936, 64)
+    assert ws >= 16 * 38 * (64 + 256) * 8
+    assert bd.ddtree_tree_attn_workspace_bytes(65, 32, 4, 128, 4096) > 0
+    # a single split needs no workspace
+    assert bd.ddtree_tree_attn_workspace_bytes(1, 1, 1, 64, 0) == 0
+    for args in [(0, 10, 1), (1, 10, 11), (33, 10, 1), (1, 5000, 1025)]:
+        with pytest.raises(bd.DDTreeError):
+            bd.ddtree_topk_workspace_bytes(*args)
+    with pytest.raises(bd.DDTreeError):
+        bd.ddtree_tree_attn_workspace_bytes(65, 30, 4, 128, 4096)  # Hq % Hkv
+    with pytest.raises(bd.DDTreeError):
+        bd.ddtree_tree_attn_workspace_bytes(65, 32, 4, 96, 4096)   # D
+
+
+def P(v):
+    return ctypes.c_void_p(v)
+
+
+FAKE = 0x1000  # a 16-byte aligned non-null value; never dereferenced on error paths
+
+
+def test_topk_validation(lib):
+    f = lib.ddtree_topk
+    assert f(P(FAKE), 1000, 4, 1000, 8, P(FAKE), P(FAKE), P(FAKE), 0, None) == bd.DDTREE_ERR_WORKSPACE_TOO_SMALL
+    assert f(None, 1000, 4, 1000, 8, P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert f(P(FAKE), 999, 4, 1000, 8, P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert f(P(FAKE), 1000, 4, 1000, 1001, P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert f(P(FAKE), 1000, 33, 1000, 8, P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == bd.DDTREE_ERR_UNSUPPORTED
+
+
+def test_build_validation(lib):
+    f = lib.ddtree_build
+    ok = [P(FAKE)] * 2
+    outs = [P(FAKE)] * 5
+    # B larger than the number of prefixes (K=2, L=2 -> 6)
+    assert f(*ok, 2, 2, 7, P(FAKE), *outs, 1, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    # mask words too few for N = 65
+    assert f(*ok, 16, 64, 64, P(FAKE), *outs, 2, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert f(*ok, 16, 64, 1025, P(FAKE), *outs, 33, None) == bd.DDTREE_ERR_UNSUPPORTED
+    assert f(*ok, 16, 64, 64, None, *outs, 3, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+
+
+def test_attn_validation(lib):
+    f = lib.ddtree_tree_attn
+    args = lambda **kw: [kw.get("q", P(FAKE)), P(FAKE), P(FAKE), kw.get("S", 4096),
+                         kw.get("S_cap", 4161), kw.get("N", 65), 32, 4, kw.get("D", 128),
+                         ctypes.c_float(kw.get("scale", 0.088)), P(FAKE), kw.get("W", 3),
+                         P(FAKE), P(FAKE), kw.get("ws", 0), None]
+    assert f(*args()) == bd.DDTREE_ERR_WORKSPACE_TOO_SMALL
+    assert f(*args(S_cap=4160, ws=1 << 40)) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert f(*args(W=2, ws=1 << 40)) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert f(*args(q=P(FAKE + 2), ws=1 << 40)) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert f(*args(D=96, ws=1 << 40)) == bd.DDTREE_ERR_UNSUPPORTED
+    assert f(*args(scale=-1.0, ws=1 << 40)) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert f(*args(N=1026, S_cap=1 << 20, W=40, ws=1 << 40)) == bd.DDTREE_ERR_UNSUPPORTED
+
+
+def test_walk_and_compact_validation(lib):
+    w = lib.ddtree_accept_walk
+    assert w(P(FAKE), P(FAKE), 65, 33, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == bd.DDTREE_ERR_UNSUPPORTED
+    assert w(P(FAKE), P(FAKE), 0, 16, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert w(P(FAKE), None, 65, 16, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    c = lib.ddtree_kv_compact
+    assert c(P(FAKE), 48, 4, 4160, 128, 4096, 65, 16, P(FAKE), P(FAKE), None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert c(P(FAKE), 48, 4, 4161, 96, 4096, 65, 16, P(FAKE), P(FAKE), None) == bd.DDTREE_ERR_UNSUPPORTED
+    assert c(P(FAKE + 8), 48, 4, 4161, 128, 4096, 65, 16, P(FAKE), P(FAKE), None) == bd.DDTREE_ERR_INVALID_ARGUMENT

@@ -1,0 +1,132 @@
+"""GPU parity: ddtree_tree_attn against the naive fp64 oracle.
+
+Element-wise bound |gpu - oracle| <= 2e-2 + 1e-2 * |oracle| (bf16 inputs,
+fp32 accumulation, bf16 softmax weights in the P.V product, bf16 output).
+Small shapes compare every output; the full workload shapes compare a
+sample of (node, head) rows the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_draft_ddtree_amd import binding as bd
+from block_diffusion_draft_ddtree_amd import synth
+from oracle import attention as oa
+from oracle import softmax_topk as st
+from oracle import tree as ot
+
+from gpu_helpers import assert_attn_close, down_bf16_bits, down_bf16_f32, say, up, up_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _tree_anc(kind, N, g, W=None):
+    if kind == "chain":
+        parent = [-1] + list(range(N - 1))
+    elif kind == "star":
+        parent = [-1] + [0] * (N - 1)
+    else:  # random recursive tree
+        parent = [-1] + [int(g.integers(0, n)) for n in range(1, N)]
+    return ot.ancestor_mask(parent, W)
+
+
+def _run(q_bits, q, kv_bits, kv, S, anc, scale=None, nodes=None, heads=None, twice=False):
+    N, Hq, D = q.shape
+    Hkv, S_cap = kv.shape[1], kv.shape[2]
+    say(f"attn N={N} Hq={Hq} Hkv={Hkv} D={D} S={S} S_cap={S_cap}")
+    qd = up_bf16(q_bits)
+    kvd = up_bf16(kv_bits)
+    ancd = up(anc.view(np.int32))
+    out = bd.ddtree_tree_attn(qd, kvd[0], kvd[1], S, ancd, scale)
+    got = down_bf16_f32(out)
+    ref = oa.tree_attention(q, kv[0], kv[1], S, anc, scale, nodes=nodes, heads=heads)
+    if nodes is not None or heads is not None:
+        nn = list(range(N)) if nodes is None else list(nodes)
+        hh = list(range(Hq)) if heads is None else list(heads)
+        got, ref = got[np.ix_(nn, hh)], ref[np.ix_(nn, hh)]
+    stats = assert_attn_close(got, ref, f"N={N} Hq={Hq} Hkv={Hkv} D={D} S={S}")
+    if twice:
+        again = bd.ddtree_tree_attn(qd, kvd[0], kvd[1], S, ancd, scale)
+        np.testing.assert_array_equal(down_bf16_bits(again), down_bf16_bits(out))
+    return stats
+
+
+def _inputs(N, Hq, Hkv, D, S, seed, S_cap=None):
+    g = synth.rng("test", 700 + seed, 1)
+    S_cap = S + N if S_cap is None else S_cap
+    q_bits, q = synth.normal_bf16(g, (N, Hq, D))
+    kv_bits, kv = synth.normal_bf16(g, (2, Hkv, S_cap, D))
+    return q_bits, q, kv_bits, kv, g
+
+
+def test_tiny_workload():
+    w = synth.TINY
+    lg = synth.drafter_logits(w)
+    lp, tok = st.topk(lg.x, w.K)
+    tree = ot.build_tree(lp.astype(np.float32), tok, w.B, 0)
+    qkv = synth.attention_inputs(w)
+    _run(qkv.q_bits, qkv.q, qkv.kv_bits[0], qkv.kv[0], w.S, tree.anc, twice=True)
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,D,S,kind", [
+    (1, 4, 2, 64, 128, "chain"),      # decode: one node
+    (17, 4, 2, 64, 0, "random"),      # no prefix at all
+    (33, 8, 2, 128, 100, "random"),   # ragged prefix (not a multiple of 64)
+    (65, 8, 1, 128, 64, "chain"),
+    (65, 16, 4, 64, 37, "star"),
+    (130, 4, 4, 128, 300, "random"),  # G = 1
+    (257, 32, 8, 128, 513, "random"),
+    (513, 4, 1, 64, 700, "random"),
+])
+def test_shapes_and_masks(N, Hq, Hkv, D, S, kind):
+    q_bits, q, kv_bits, kv, g = _inputs(N, Hq, Hkv, D, S, N + S + D)
+    anc = _tree_anc(kind, N, g)
+    _run(q_bits, q, kv_bits, kv, S, anc, twice=True)
+
+
+def test_slack_capacity_and_extra_mask_words():
+    N, Hq, Hkv, D, S = 40, 8, 2, 128, 190
+    q_bits, q, kv_bits, kv, g = _inputs(N, Hq, Hkv, D, S, 1, S_cap=S + N + 77)
+    anc = _tree_anc("random", N, g, W=5)
+    _run(q_bits, q, kv_bits, kv, S, anc, scale=0.05)
+
+
+def test_planted_keys_order_one_outputs():
+    """Queries parallel to one visible key with a large scale: the output is
+    that key's value row, an O(1) signal the tolerance can see."""
+    N, Hq, Hkv, D, S = 9, 4, 2, 64, 70
+    q_bits, q, kv_bits, kv, g = _inputs(N, Hq, Hkv, D, S, 2)
+    parent = [-1, 0, 1, 2, 0, 4, 5, 1, 7]
+    anc = ot.ancestor_mask(parent)
+    kv = kv.copy()
+    G = Hq // Hkv
+    for n in range(N):
+        for h in range(Hq):
+            target = S + parent[n] if n else 3  # parent's tree row, or a prefix row
+            kv[0, h // G, target] = q[n, h]
+    kv_bits = synth.f32_to_bf16_bits(kv)
+    kv = synth.bf16_bits_to_f32(kv_bits)
+    _run(q_bits, q, kv_bits, kv, S, anc, scale=2.0)
+
+
+@pytest.mark.parametrize("name", ["coder30b_b64", "qwen3_8b", "coder30b_b256"])
+def test_full_workload_sampled(name):
+    w = synth.WORKLOADS[name]
+    lg = synth.drafter_logits(w)
+    lp, tok = st.topk(lg.x, w.K)
+    tree = ot.build_tree(lp.astype(np.float32), tok, w.B, 0)
+    qkv = synth.attention_inputs(w, layers=1)
+    g = synth.rng("test", 790, 0)
+    nodes = sorted(set([0, w.N - 1] + g.choice(w.N, 6, replace=False).tolist()))
+    heads = sorted(set([0, w.Hq - 1] + g.choice(w.Hq, 3, replace=False).tolist()))
+    _run(qkv.q_bits, qkv.q, qkv.kv_bits[0], qkv.kv[0], w.S, tree.anc, nodes=nodes, heads=heads)
+
+
+def test_long_context_sampled():
+    w = synth.LONGCTX
+    lg = synth.drafter_logits(w)
+    lp, tok = st.topk(lg.x, w.K)
+    tree = ot.build_tree(lp.astype(np.float32), tok, w.B, 0)
+    qkv = synth.attention_inputs(w, layers=1)
+    nodes = [0, 1, 100, 256]
+    heads = [0, 13, 31]
+    _run(qkv.q_bits, qkv.q, qkv.kv_bits[0], qkv.kv[0], w.S, tree.anc, nodes=nodes, heads=heads)

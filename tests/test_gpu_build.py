@@ -1,0 +1,109 @@
+"""GPU parity: ddtree_build against the oracle tree, bit for bit.
+
+Both sides take the identical fp32 [L, K] table (either a synthetic sorted
+table or the GPU top-K output downloaded), so parent, depth, token, score
+(compared as bits) and the packed ancestor mask must be equal exactly."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_draft_ddtree_amd import binding as bd
+from block_diffusion_draft_ddtree_amd import synth
+from oracle import softmax_topk as st
+from oracle import tree as ot
+
+from gpu_helpers import down, say, up
+
+pytestmark = pytest.mark.gpu
+
+ROOT_TOKEN = 4242
+
+
+def _gpu_tree(lp32, tok, B, W=None):
+    L, K = lp32.shape
+    say(f"build L={L} K={K} B={B} W={W}")
+    root = up(np.array([ROOT_TOKEN], dtype=np.int32))
+    out = bd.ddtree_build(up(lp32), up(tok.astype(np.int32)), B, root, mask_words=W)
+    return [down(t) for t in out]
+
+
+def _compare(lp32, tok, B, W=None, twice=False):
+    lp32 = np.ascontiguousarray(lp32, dtype=np.float32)
+    parent, depth, ntok, score, anc = _gpu_tree(lp32, tok, B, W)
+    ref = ot.build_tree(lp32, tok, B, ROOT_TOKEN, mask_words=W)
+    np.testing.assert_array_equal(parent, ref.parent)
+    np.testing.assert_array_equal(depth, ref.depth)
+    np.testing.assert_array_equal(ntok, ref.token)
+    np.testing.assert_array_equal(score.view(np.uint32), ref.score.view(np.uint32))
+    np.testing.assert_array_equal(anc.view(np.uint32), ref.anc)
+    if twice:
+        again = _gpu_tree(lp32, tok, B, W)
+        for a, b in zip(again, (parent, depth, ntok, score, anc)):
+            np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+    return ref
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("ties", [False, True])
+def test_random_tables(seed, ties):
+    g = synth.rng("test", 600 + seed, int(ties))
+    L = int(g.integers(1, 7))
+    K = int(g.integers(1, 9))
+    lp, tok = synth.sorted_logp_table(L, K, 1000, g, scale=float(g.uniform(0.1, 2.0)), ties=ties)
+    total = ot.num_prefixes(L, K)
+    for B in sorted({1, min(total, 7), min(total, 64), min(total, 300)}):
+        _compare(lp, tok, B, twice=(B == 64))
+
+
+def test_tiny_workload_from_gpu_topk():
+    w = synth.TINY
+    x = synth.drafter_logits(w).x
+    say("tiny topk for build")
+    lp, tok = bd.ddtree_topk(up(x), w.K)
+    lp32, tok = down(lp), down(tok)
+    _compare(lp32, tok, w.B, twice=True)
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b", "coder30b_b64", "coder30b_b256", "sweep_b512"])
+def test_full_workloads_from_gpu_topk(name):
+    w = synth.WORKLOADS[name]
+    x = synth.drafter_logits(w).x
+    say(f"{name} topk for build")
+    lp, tok = bd.ddtree_topk(up(x), w.K)
+    ref = _compare(down(lp), down(tok), w.B)
+    assert ref.N == w.N
+
+
+@pytest.mark.parametrize("B", [40, 200, 1024])
+def test_deep_trees(B):
+    g = synth.rng("test", 610, B)
+    x = synth.deep_logits(16, 500, g)
+    lp, tok = st.topk(x, 8)
+    ref = _compare(lp.astype(np.float32), tok, B, twice=True)
+    assert ref.depth.max() >= 5
+
+
+def test_special_cases():
+    g = synth.rng("test", 620, 0)
+    lp, tok = synth.sorted_logp_table(16, 1, 1000, g)
+    ref = _compare(lp, tok, 16)               # K = 1: a chain of depth L
+    assert ref.parent.tolist() == [-1] + list(range(16))
+    lp, tok = synth.sorted_logp_table(3, 4, 1000, g)
+    _compare(lp, tok, ot.num_prefixes(3, 4))  # complete tree
+    _compare(lp, tok, 1)                      # one node
+    _compare(lp, tok, 20, W=4)                # extra mask words stay zero
+
+
+def test_certain_positions_child_ties_parent():
+    """log-prob 0 at a position makes a child tie its parent exactly."""
+    lp = np.array([[-0.5, -1.0, -1.0], [0.0, -2.0, -3.0], [0.0, 0.0, -1.0]], dtype=np.float32)
+    tok = np.arange(9, dtype=np.int32).reshape(3, 3)
+    _compare(lp, tok, 25, twice=True)
+
+
+def test_max_table():
+    g = synth.rng("test", 630, 0)
+    lp, tok = synth.sorted_logp_table(32, 16, 100000, g, scale=0.3)
+    _compare(lp, tok, 1024)
+    lp, tok = synth.sorted_logp_table(16, 1024, 200000, g, scale=3.0)
+    _compare(lp, tok, 64)

@@ -1,0 +1,88 @@
+"""GPU parity: ddtree_topk against the oracle's log-softmax and top-K.
+
+Token ids must match exactly, in rank order (ties by smaller id); log-probs
+within 1e-5 absolute of the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_draft_ddtree_amd import binding as bd
+from block_diffusion_draft_ddtree_amd import synth
+from oracle import softmax_topk as st
+
+from gpu_helpers import LOGP_ATOL, down, say, up
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(x: np.ndarray, K: int, stride: int | None = None, twice: bool = True,
+           lp_atol: float = LOGP_ATOL):
+    L, V = x.shape
+    if stride is not None and stride > V:
+        buf = np.full((L, stride), 1e30, dtype=np.float32)  # poison beyond V
+        buf[:, :V] = x
+        dev = up(buf)[:, :V]
+    else:
+        dev = up(x)
+    say(f"topk L={L} V={V} K={K} stride={stride}")
+    lp, tok = bd.ddtree_topk(dev, K)
+    lp_g, tok_g = down(lp), down(tok)
+    ref_lp, ref_tok = st.topk(x, K)
+    np.testing.assert_array_equal(tok_g, ref_tok)
+    assert np.abs(lp_g.astype(np.float64) - ref_lp).max() <= lp_atol
+    if twice:
+        lp2, tok2 = bd.ddtree_topk(dev, K)
+        np.testing.assert_array_equal(down(tok2), tok_g)
+        np.testing.assert_array_equal(down(lp2).view(np.uint32), lp_g.view(np.uint32))
+    return lp_g, tok_g
+
+
+def test_tiny_workload():
+    w = synth.TINY
+    _check(synth.drafter_logits(w).x, w.K)
+
+
+@pytest.mark.parametrize("name,K", [("qwen3_8b", 64), ("coder30b_b256", 256), ("sweep_b16", 16),
+                                    ("sweep_b512", 512)])
+def test_full_vocab_workloads(name, K):
+    w = synth.WORKLOADS[name]
+    _check(synth.drafter_logits(w).x, K)
+
+
+def test_ties_smaller_id_first():
+    g = synth.rng("test", 500, 0)
+    x = synth.tie_logits(3, 20000, g, levels=4)
+    _check(x, 100)
+    _check(x, 1024)
+
+
+def test_signed_zero_and_few_values():
+    x = np.zeros((2, 5000), dtype=np.float32)
+    x[0, ::3] = -0.0
+    x[1, 7] = 1.0
+    _check(x, 37)
+
+
+@pytest.mark.parametrize("V,K", [(1, 1), (7, 7), (300, 300), (4097, 1), (4096, 4096 // 4),
+                                 (8193, 1024), (151936, 1)])
+def test_edge_shapes(V, K):
+    g = synth.rng("test", 501, V)
+    x = (2.0 * g.standard_normal((3, V))).astype(np.float32)
+    _check(x, min(K, V))
+
+
+def test_row_stride_and_max_rows():
+    g = synth.rng("test", 502, 0)
+    x = (1.5 * g.standard_normal((32, 9000))).astype(np.float32)
+    _check(x, 200, stride=9216)
+
+
+def test_wide_spread_logits():
+    """Values spread over many octaves exercise the far bins of the first digit.
+    Log-probs reach about -3000 here, where one fp32 ulp is 2.4e-4, so the
+    log-prob bound is 4 ulp of the largest magnitude instead of 1e-5."""
+    g = synth.rng("test", 503, 0)
+    x = (g.standard_normal((4, 50000)) * np.exp(g.uniform(-3, 6, (4, 50000)))).astype(np.float32)
+    ref, _ = st.topk(x, 700)
+    tol = 4 * float(np.spacing(np.float32(np.abs(ref).max())))
+    _check(x, 700, lp_atol=tol)
