@@ -31,6 +31,7 @@ int topk_check(int L, int V, int K) {
   if (L < 1 || V < 1 || K < 1) return DDTREE_ERR_INVALID_ARGUMENT;
   if (K > V) return DDTREE_ERR_INVALID_ARGUMENT;
   if (L > DDTREE_MAX_L || K > DDTREE_MAX_K) return DDTREE_ERR_UNSUPPORTED;
+  if (V > DDTREE_MAX_V) return DDTREE_ERR_UNSUPPORTED;
   return DDTREE_OK;
 }
 

@@ -10,12 +10,18 @@
 // root) owns exactly one "slot" that holds its next not-yet-popped child:
 // popping slot p's candidate creates node b, advances slot p to its next
 // sibling rank and opens slot b at child rank 0. So the frontier is an
-// array of at most B + 1 slots indexed by node id; slot n lives in lane
-// n & 63, register n >> 6 of wave 0, as the 32-bit order key of its
-// candidate's fp32 score. A pop is a wave-wide max of the lanes' local
-// maxima (shuffle butterfly) plus a ballot; exact score ties fall back to a
+// array of at most B + 1 slots indexed by node id. Slot n lives in lane
+// n & 63, register n >> 6 of wave 0, which keeps everything about it in
+// registers: its candidate's order key and fp32 score, the candidate's
+// rank, the node's own score, depth, parent and rank, and the log-prob of
+// the candidate after the current one (prefetched from LDS so that
+// advancing a slot never waits on memory).
+//
+// A pop: each lane takes the max key over its slots, a DPP max inside each
+// 16-lane row plus four readlanes gives the wave max in a scalar register,
+// and a ballot finds the owner. Exact score ties fall back to a
 // wave-cooperative lexicographic comparison of the rank tuples, which are
-// rebuilt from the parent/rank arrays in LDS.
+// rebuilt from parent/rank arrays kept in LDS.
 //
 // Scores follow the fp32 left-to-right sum: a depth-1 candidate is logp[0][r]
 // itself, deeper ones fl(score(parent) + logp[d][r]).
@@ -28,15 +34,43 @@ constexpr int kMaxN = DDTREE_MAX_B + 1;
 
 struct BuildLds {
   float lp[DDTREE_MAX_LK];
-  float score[kMaxN];
-  float cscore[kMaxN];  // score of the slot's current candidate
   int16_t parent[kMaxN];
-  int16_t rank[kMaxN];   // last rank of the node's tuple
-  int16_t crank[kMaxN];  // rank of the slot's current candidate
+  int16_t rank[kMaxN];
   uint8_t depth[kMaxN];
 };
 
-__device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memory"); }
+// DPP controls (gfx9 encoding).
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
+constexpr int kRowMirror = 0x140;      // lane i <-> 15 - i within each 16 lanes
+
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v, int ctrl_id) {
+  uint32_t o;
+  switch (ctrl_id) {
+    case 0: o = __builtin_amdgcn_update_dpp(v, v, kQuadXor1, 0xF, 0xF, false); break;
+    case 1: o = __builtin_amdgcn_update_dpp(v, v, kQuadXor2, 0xF, 0xF, false); break;
+    case 2: o = __builtin_amdgcn_update_dpp(v, v, kRowHalfMirror, 0xF, 0xF, false); break;
+    default: o = __builtin_amdgcn_update_dpp(v, v, kRowMirror, 0xF, 0xF, false); break;
+  }
+  return o > v ? o : v;
+}
+
+// Wave-wide max, returned in a scalar (uniform) register.
+__device__ __forceinline__ uint32_t wave_umax_uniform(uint32_t v) {
+  v = dpp_umax(v, 0);
+  v = dpp_umax(v, 1);
+  v = dpp_umax(v, 2);
+  v = dpp_umax(v, 3);  // every lane now holds the max of its 16-lane row
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), lane));
+}
 
 // Rank at depth `d` (1-based) of the tuple of node `x` (depth(x) >= d).
 __device__ __forceinline__ int rank_at(const BuildLds& s, int x, int d) {
@@ -44,14 +78,14 @@ __device__ __forceinline__ int rank_at(const BuildLds& s, int x, int d) {
   return s.rank[x];
 }
 
-// Wave-uniform: is the candidate of slot a lexicographically before the
-// candidate of slot b? Lane i holds element i of each rank tuple.
-__device__ bool cand_lex_less(const BuildLds& s, int a, int b) {
+// Wave-uniform: is candidate (slot a, rank ca) lexicographically before
+// candidate (slot b, rank cb)? Lane i holds element i of each rank tuple.
+__device__ bool cand_lex_less(const BuildLds& s, int a, int ca, int b, int cb) {
   const int lane = ddt::lane_id();
   const int da = s.depth[a] + 1, db = s.depth[b] + 1;
   int xa = -1, xb = -1;
-  if (lane < da) xa = (lane == da - 1) ? (int)s.crank[a] : rank_at(s, a, lane + 1);
-  if (lane < db) xb = (lane == db - 1) ? (int)s.crank[b] : rank_at(s, b, lane + 1);
+  if (lane < da) xa = (lane == da - 1) ? ca : rank_at(s, a, lane + 1);
+  if (lane < db) xb = (lane == db - 1) ? cb : rank_at(s, b, lane + 1);
   const uint64_t diff = ddt::ballot(xa != xb);
   if (!diff) return a < b;  // identical tuples cannot occur
   const int f = __ffsll((unsigned long long)diff) - 1;
@@ -63,85 +97,134 @@ __device__ bool cand_lex_less(const BuildLds& s, int a, int b) {
 template <int J>
 __device__ void pop_loop(BuildLds& s, int L, int K, int B) {
   const int lane = ddt::lane_id();
-  uint32_t rk[J];
+  // Per-slot state (slot n = lane + 64 * j).
+  uint32_t key[J];   // order key of the candidate's score, 0 = no candidate
+  float csc[J];      // candidate score
+  int crk[J];        // candidate rank
+  float nlp[J];      // log-prob of the following sibling candidate
+  float nsc[J];      // the node's own score
+  int dep[J];        // the node's depth
 #pragma unroll
-  for (int j = 0; j < J; ++j) rk[j] = 0u;
-  if (lane == 0) rk[0] = ddt::f32_key(s.cscore[0]);
+  for (int j = 0; j < J; ++j) {
+    key[j] = 0u;
+    csc[j] = 0.f;
+    crk[j] = 0;
+    nlp[j] = 0.f;
+    nsc[j] = 0.f;
+    dep[j] = 0;
+  }
+  // Lane d (< L) holds logp[d][0]: the first child's log-prob at depth d + 1.
+  const float row0 = lane < L ? s.lp[lane * K] : 0.f;
+  if (lane == 0) {
+    csc[0] = s.lp[0];
+    key[0] = ddt::f32_key(csc[0]);
+    nlp[0] = K > 1 ? s.lp[1] : 0.f;
+  }
 
   for (int b = 1; b <= B; ++b) {
-    // Local maximum over this lane's slots.
     uint32_t lk = 0u;
     int lj = 0;
     bool ltie = false;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      if (rk[j] > lk) {
-        lk = rk[j];
+      if (key[j] > lk) {
+        lk = key[j];
         lj = j;
         ltie = false;
-      } else if (rk[j] == lk && lk != 0u) {
+      } else if (key[j] == lk && lk != 0u) {
         ltie = true;
       }
     }
-    const uint32_t kmax = ddt::wave_max_u32(lk);
+    const uint32_t kmax = wave_umax_uniform(lk);
     const uint64_t hit = ddt::ballot(lk == kmax);
     const uint64_t tie = ddt::ballot(lk == kmax && ltie);
     int p;
     if (__popcll(hit) == 1 && tie == 0) {
       const int wl = __ffsll((unsigned long long)hit) - 1;
-      p = __shfl(lane + 64 * lj, wl, 64);
+      p = wl + 64 * __builtin_amdgcn_readlane(lj, wl);
     } else {
       // Several slots share the best score: smallest rank tuple wins.
       p = -1;
+      int pc = 0;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        uint64_t m = ddt::ballot(rk[j] == kmax);
+        uint64_t m = ddt::ballot(key[j] == kmax);
         while (m) {
           const int l = __ffsll((unsigned long long)m) - 1;
           m &= m - 1;
           const int cand = l + 64 * j;
-          if (p < 0 || cand_lex_less(s, cand, p)) p = cand;
+          const int cc = __builtin_amdgcn_readlane(crk[j], l);
+          if (p < 0 || cand_lex_less(s, cand, cc, p, pc)) {
+            p = cand;
+            pc = cc;
+          }
         }
       }
     }
     p = __builtin_amdgcn_readfirstlane(p);
+    const int pl = p & 63, pj = p >> 6;
 
-    const int c = s.crank[p];
-    const float sc = s.cscore[p];
-    const int dp = s.depth[p];
+    // Gather slot p's state from its owner lane.
+    int c = 0, dp = 0;
+    float sc = 0.f, nl = 0.f, ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (j == pj) {
+        c = __builtin_amdgcn_readlane(crk[j], pl);
+        dp = __builtin_amdgcn_readlane(dep[j], pl);
+        sc = readlane_f(csc[j], pl);
+        nl = readlane_f(nlp[j], pl);
+        ps = readlane_f(nsc[j], pl);
+      }
+    }
     const int dn = dp + 1;
-    // Advance slot p to its next sibling.
-    const int c2 = c + 1;
-    uint32_t pk = 0u;
-    float ps = 0.f;
-    if (c2 < K) {
-      ps = (dp == 0) ? s.lp[c2] : (s.score[p] + s.lp[dp * K + c2]);
-      pk = ddt::f32_key(ps);
-    }
-    // Open slot b at its first child.
-    uint32_t bk = 0u;
-    float bs = 0.f;
-    if (dn < L) {
-      bs = sc + s.lp[dn * K];
-      bk = ddt::f32_key(bs);
-    }
-    compiler_fence();
     if (lane == 0) {
       s.parent[b] = (int16_t)p;
       s.rank[b] = (int16_t)c;
       s.depth[b] = (uint8_t)dn;
-      s.score[b] = sc;
-      s.crank[p] = (int16_t)c2;
-      s.cscore[p] = ps;
-      s.crank[b] = 0;
-      s.cscore[b] = bs;
     }
-    compiler_fence();
+    // Advance slot p to its next sibling (rank c + 1, log-prob prefetched).
+    const int c2 = c + 1;
+    float ps2 = 0.f;
+    uint32_t pk = 0u;
+    if (c2 < K) {
+      ps2 = (dp == 0) ? nl : (ps + nl);
+      pk = ddt::f32_key(ps2);
+    }
+    const float nl2 = (c2 + 1 < K) ? s.lp[dp * K + c2 + 1] : 0.f;
+    // Open slot b at its first child.
+    uint32_t bk = 0u;
+    float bs = 0.f;
+    if (dn < L) {
+      bs = sc + readlane_f(row0, dn);
+      bk = ddt::f32_key(bs);
+    }
+    const float bnl = (dn < L && K > 1) ? s.lp[dn * K + 1] : 0.f;
+    const int bl = b & 63, bj = b >> 6;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      if (lane == (p & 63) && j == (p >> 6)) rk[j] = pk;
-      if (lane == (b & 63) && j == (b >> 6)) rk[j] = bk;
+      if (lane == pl && j == pj) {
+        key[j] = pk;
+        csc[j] = ps2;
+        crk[j] = c2;
+        nlp[j] = nl2;
+      }
+      if (lane == bl && j == bj) {
+        key[j] = bk;
+        csc[j] = bs;
+        crk[j] = 0;
+        nlp[j] = bnl;
+        nsc[j] = sc;
+        dep[j] = dn;
+      }
     }
+  }
+  // Node scores to LDS (the lp table is no longer needed; reuse its space).
+  float* score_out = s.lp;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int n = lane + 64 * j;
+    if (n <= B) score_out[n] = nsc[j];
   }
 }
 
@@ -159,24 +242,19 @@ __global__ __launch_bounds__(kThreads) void build_kernel(
     s.parent[0] = -1;
     s.rank[0] = 0;
     s.depth[0] = 0;
-    s.score[0] = 0.f;
-  }
-  __syncthreads();
-  if (t == 0) {
-    s.crank[0] = 0;
-    s.cscore[0] = s.lp[0];
   }
   __syncthreads();
   if (t < 64) pop_loop<J>(s, L, K, B);
   __syncthreads();
 
   const int N = B + 1;
+  const float* nscore = s.lp;
   for (int n = t; n < N; n += kThreads) {
     const int d = s.depth[n];
     parent_out[n] = s.parent[n];
     depth_out[n] = d;
     tok_out[n] = n == 0 ? *root_token : token[(d - 1) * K + s.rank[n]];
-    if (score_out) score_out[n] = s.score[n];
+    if (score_out) score_out[n] = nscore[n];
     // Ancestor-or-self row, written from the high word down.
     uint32_t* row = anc + (int64_t)n * W;
     int wcur = W - 1;

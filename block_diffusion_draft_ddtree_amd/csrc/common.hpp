@@ -53,6 +53,44 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// DPP-based reductions: a fixed butterfly inside each 16-lane row
+// (quad xor 1, quad xor 2, half-row mirror, row mirror), then the four row
+// results are read into scalar registers and combined in a fixed order.
+// The result is wave-uniform and bit-reproducible.
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i within 8 lanes
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15 - i within 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
+                                                    0xF, 0xF, false));
+}
+
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpMin {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fminf(a, b); }
+};
+struct OpSum {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+
+template <class Op>
+__device__ __forceinline__ float wave_reduce_uniform(float v, Op op) {
+  v = op(v, dpp_f32<kDppQuadXor1>(v));
+  v = op(v, dpp_f32<kDppQuadXor2>(v));
+  v = op(v, dpp_f32<kDppRowHalfMirror>(v));
+  v = op(v, dpp_f32<kDppRowMirror>(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return op(op(a, b), op(c, d));
+}
+
 // Ballot across the wave as a 64-bit mask.
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 

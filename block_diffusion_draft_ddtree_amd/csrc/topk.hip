@@ -5,19 +5,23 @@
 //   chunk kernel  grid (C chunks, L rows), 256 threads, 4096 logits per
 //                 workgroup held in registers (16 per thread, coalesced
 //                 dword loads: one HBM pass). Emits the chunk's (max,
-//                 sum-exp) pair and a candidate superset of the chunk's top-K.
+//                 sum-exp) pair, a candidate superset of the chunk's top-K
+//                 and a lower bound t_c of the chunk's K-th largest logit
+//                 (the smallest candidate; -inf for chunks shorter than K).
 //   merge kernel  grid L, 1024 threads. Combines the (max, sum) pairs into
-//                 lse, selects the exact top-K among the candidates, ranks
-//                 them and writes logp = x - lse and the token ids.
+//                 lse, keeps the candidates >= tau = max_c t_c (a valid
+//                 lower bound of the row's K-th largest, so every top-K
+//                 element survives), ranks the survivors exactly in LDS and
+//                 writes logp = x - lse and the token ids in rank order.
 //
 // Selection is a radix select. Its first digit is relative to the reference
 // maximum m: digit = bits(fl(m - x) + 1) >> 19, clamped (16 bins per octave
 // of the distance below the max), which spreads the few values near the top
-// over many bins and keeps LDS atomic contention low. The boundary bin is
-// then refined on the exact fp32 order key (4 x 8 bits) and, for exact ties,
-// on the token index (smaller id first). The chunk kernel may stop after the
-// first digit when the candidate set fits its slots ("loose" mode); the
-// merge kernel always resolves exactly.
+// over many bins and keeps LDS atomic contention low; it is monotone in x.
+// The boundary bin is refined on the exact fp32 order key (4 x 8 bits) and,
+// for exact ties, on the index (smaller id first). The chunk kernel stops
+// after the first digit when the candidate set fits its slots ("loose").
+// Ranking is by (logit descending, token id ascending) throughout.
 #include "common.hpp"
 
 namespace {
@@ -27,6 +31,8 @@ constexpr int kPerThread = 16;
 constexpr int kChunk = kChunkThreads * kPerThread;  // 4096
 constexpr int kLooseExtra = 256;                     // slots beyond K per chunk
 constexpr int kMergeThreads = 1024;
+constexpr int kSurvCap = 8192;                       // survivors ranked in LDS
+constexpr int kLoadBatch = 8;                        // candidates loaded per thread at once
 
 // Larger digit = closer to the reference maximum (monotone in x).
 __device__ __forceinline__ uint32_t rel_digit(float ref_max, float x) {
@@ -34,6 +40,11 @@ __device__ __forceinline__ uint32_t rel_digit(float ref_max, float x) {
   uint32_t b = (__float_as_uint(y) - 0x3F800000u) >> 19;
   b = b > 255u ? 255u : b;
   return 255u - b;
+}
+
+// a before b in rank order: larger logit first, then smaller id.
+__device__ __forceinline__ bool beats(float xa, int ia, float xb, int ib) {
+  return xa > xb || (xa == xb && ia < ib);
 }
 
 struct SelShared {
@@ -84,34 +95,70 @@ __device__ void find_digit(SelShared& s, uint32_t need) {
   __syncthreads();
 }
 
-__device__ __forceinline__ float block_max_256(float v, float* red) {
-  v = ddt::wave_max_f32(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+// Exact threshold inside the boundary bucket d0 of the relative digit:
+// elements of that bucket are taken iff (key > tkey) or (key == tkey and
+// ikey(index) >= tik), where ikey is larger for smaller indices. ACTIVE(i)
+// says whether element i is in the bucket; KEY(i), IKEY(i) give its keys.
+// All threads call this; ends with every thread holding the result.
+template <class Active, class Key, class IKey>
+__device__ __forceinline__ void refine_bucket(SelShared& sh, uint32_t need, int n_elems, int idx_passes,
+                              Active active, Key keyf, IKey ikeyf, uint32_t& tkey,
+                              uint32_t& tik) {
+  uint32_t prefix = 0u, mask = 0u, inb = 0u;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    __syncthreads();
+    zero_hist(sh);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < n_elems; ++i) {
+      if (active(i)) {
+        const uint32_t k = keyf(i);
+        if ((k & mask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    find_digit(sh, need);
+    prefix |= sh.digit << shift;
+    mask |= 255u << shift;
+    need = sh.need;
+    inb = sh.in_bin;
+  }
+  tkey = prefix;
+  tik = 0u;
+  if (need < inb) {
+    uint32_t ip = 0u, im = 0u;
+    for (int shift = 8 * (idx_passes - 1); shift >= 0; shift -= 8) {
+      __syncthreads();
+      zero_hist(sh);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < n_elems; ++i) {
+        if (active(i) && keyf(i) == tkey) {
+          const uint32_t ik = ikeyf(i);
+          if ((ik & im) == ip) atomicAdd(&sh.hist[(ik >> shift) & 255u], 1u);
+        }
+      }
+      __syncthreads();
+      find_digit(sh, need);
+      ip |= sh.digit << shift;
+      im |= 255u << shift;
+      need = sh.need;
+    }
+    tik = ip;
+  }
   __syncthreads();
-  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return r;
-}
-
-__device__ __forceinline__ float block_sum_256(float v, float* red) {
-  v = ddt::wave_sum_f32(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const float r = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
-  return r;
 }
 
 __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
     const float* __restrict__ logits, int64_t stride, int V, int K, int cap,
-    float2* __restrict__ stats, int* __restrict__ counts,
-    float* __restrict__ cand_x, int* __restrict__ cand_i) {
+    float4* __restrict__ stats, int* __restrict__ counts, float* __restrict__ cand_x,
+    int* __restrict__ cand_i) {
   __shared__ SelShared sh;
-  __shared__ float red[4];
+  __shared__ float red[3][4];
   const int chunk = blockIdx.x, row = blockIdx.y, C = gridDim.x;
   const int base = chunk * kChunk;
   const int n = min(kChunk, V - base);
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const float* src = logits + (int64_t)row * stride + base;
 
   float x[kPerThread];
@@ -120,79 +167,47 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
     const int e = t + kChunkThreads * j;
     x[j] = e < n ? src[e] : -INFINITY;
   }
+  zero_hist(sh);
   if (t == 0) sh.out_count = 0u;
 
-  float m = -INFINITY;
+  float mx = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) m = fmaxf(m, x[j]);
-  m = block_max_256(m, red);
+  for (int j = 0; j < kPerThread; ++j) mx = fmaxf(mx, x[j]);
+  mx = ddt::wave_reduce_uniform(mx, ddt::OpMax());
+  if (lane == 0) red[0][wave] = mx;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+
   float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j)
-    if (t + kChunkThreads * j < n) s += __expf(x[j] - m);
-  s = block_sum_256(s, red);
-
-  const uint32_t Kc = (uint32_t)min(K, n);
-
-  // Pass 0: distance-to-max digit.
-  zero_hist(sh);
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j)
-    if (t + kChunkThreads * j < n) atomicAdd(&sh.hist[rel_digit(m, x[j])], 1u);
-  __syncthreads();
-  find_digit(sh, Kc);
-  const uint32_t d0 = sh.digit;
-  uint32_t need = sh.need;
-  const bool loose = sh.above + sh.in_bin <= (uint32_t)cap;
-  bool take_bin = loose || need == sh.in_bin;
-  uint32_t tkey = 0u, tik = 0u;
-  if (!take_bin) {
-    uint32_t prefix = 0u, mask = 0u, inb = 0u;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      __syncthreads();
-      zero_hist(sh);
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) {
-        if (t + kChunkThreads * j < n && rel_digit(m, x[j]) == d0) {
-          const uint32_t k = ddt::f32_key(x[j]);
-          if ((k & mask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
-        }
-      }
-      __syncthreads();
-      find_digit(sh, need);
-      prefix |= sh.digit << shift;
-      mask |= 255u << shift;
-      need = sh.need;
-      inb = sh.in_bin;
-    }
-    tkey = prefix;
-    if (need < inb) {
-      uint32_t ip = 0u, im = 0u;
-      for (int shift = 8; shift >= 0; shift -= 8) {
-        __syncthreads();
-        zero_hist(sh);
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kPerThread; ++j) {
-          const int e = t + kChunkThreads * j;
-          if (e < n && rel_digit(m, x[j]) == d0 && ddt::f32_key(x[j]) == tkey) {
-            const uint32_t ik = 0xFFFFu - (uint32_t)e;
-            if ((ik & im) == ip) atomicAdd(&sh.hist[(ik >> shift) & 255u], 1u);
-          }
-        }
-        __syncthreads();
-        find_digit(sh, need);
-        ip |= sh.digit << shift;
-        im |= 255u << shift;
-        need = sh.need;
-      }
-      tik = ip;
+  for (int j = 0; j < kPerThread; ++j) {
+    if (t + kChunkThreads * j < n) {
+      s += __expf(x[j] - m);
+      atomicAdd(&sh.hist[rel_digit(m, x[j])], 1u);
     }
   }
+  s = ddt::wave_reduce_uniform(s, ddt::OpSum());
+  if (lane == 0) red[1][wave] = s;
+  __syncthreads();
 
-  const int64_t slot0 = ((int64_t)row * C + chunk) * cap;
+  const uint32_t Kc = (uint32_t)min(K, n);
+  find_digit(sh, Kc);
+  const uint32_t d0 = sh.digit;
+  const uint32_t need = sh.need;
+  const bool loose = sh.above + sh.in_bin <= (uint32_t)cap;
+  const bool take_bin = loose || need == sh.in_bin;
+  uint32_t tkey = 0u, tik = 0u;
+  if (!take_bin) {
+    refine_bucket(
+        sh, need, kPerThread, 2,
+        [&](int j) { return t + kChunkThreads * j < n && rel_digit(m, x[j]) == d0; },
+        [&](int j) { return ddt::f32_key(x[j]); },
+        [&](int j) { return 0xFFFFu - (uint32_t)(t + kChunkThreads * j); }, tkey, tik);
+  }
+
+  // Selection flags, one LDS atomic per wave for the output base.
+  uint32_t selmask = 0u;
+  float tmin = INFINITY;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     const int e = t + kChunkThreads * j;
@@ -210,114 +225,213 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
         }
       }
     }
-    const uint64_t bm = ddt::ballot(sel);
-    uint32_t wbase = 0u;
-    if ((t & 63) == 0 && bm) wbase = atomicAdd(&sh.out_count, (uint32_t)__popcll(bm));
-    wbase = __shfl(wbase, 0, 64);
     if (sel) {
-      const uint32_t pos = wbase + ddt::lanes_below(bm);
-      cand_x[slot0 + pos] = x[j];
-      cand_i[slot0 + pos] = base + e;
+      selmask |= 1u << j;
+      tmin = fminf(tmin, x[j]);
     }
   }
+  uint32_t wave_total = 0u;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) wave_total += (uint32_t)__popcll(ddt::ballot((selmask >> j) & 1u));
+  uint32_t wbase = 0u;
+  if (lane == 0 && wave_total) wbase = atomicAdd(&sh.out_count, wave_total);
+  wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase);
+  const int64_t slot0 = ((int64_t)row * C + chunk) * cap;
+  uint32_t run = 0u;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const bool sel = (selmask >> j) & 1u;
+    const uint64_t bm = ddt::ballot(sel);
+    if (sel) {
+      const uint32_t pos = wbase + run + ddt::lanes_below(bm);
+      cand_x[slot0 + pos] = x[j];
+      cand_i[slot0 + pos] = base + t + kChunkThreads * j;
+    }
+    run += (uint32_t)__popcll(bm);
+  }
+  tmin = ddt::wave_reduce_uniform(tmin, ddt::OpMin());
+  if (lane == 0) red[2][wave] = tmin;
   __syncthreads();
   if (t == 0) {
+    const float ssum = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    const float tc = fminf(fminf(red[2][0], red[2][1]), fminf(red[2][2], red[2][3]));
     counts[row * C + chunk] = (int)sh.out_count;
-    stats[row * C + chunk] = make_float2(m, s);
+    stats[row * C + chunk] = make_float4(m, ssum, Kc == (uint32_t)K ? tc : -INFINITY, 0.f);
   }
 }
 
+struct MergeLds {
+  SelShared sh;
+  int offs[kMergeThreads + 1];  // exclusive prefix of chunk counts (C <= 1024)
+  float sx[kSurvCap];
+  int si[kSurvCap];
+  float wx[DDTREE_MAX_K];
+  int wi[DDTREE_MAX_K];
+  float lse, tau, M;
+  int total;
+  uint32_t nsurv, nwin;
+};
+
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
-    int C, int K, int cap, int idx_passes, const float2* __restrict__ stats,
+    int C, int K, int cap, int idx_passes, const float4* __restrict__ stats,
     const int* __restrict__ counts, const float* __restrict__ cand_x,
-    const int* __restrict__ cand_i, float* __restrict__ logp,
-    int32_t* __restrict__ token) {
-  __shared__ SelShared sh;
-  __shared__ float wx[DDTREE_MAX_K];
-  __shared__ int wi[DDTREE_MAX_K];
-  __shared__ float s_lse, s_max;
-  const int row = blockIdx.x, t = threadIdx.x;
-  const float2* st = stats + (int64_t)row * C;
+    const int* __restrict__ cand_i, float* __restrict__ logp, int32_t* __restrict__ token) {
+  __shared__ MergeLds s;
+  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63;
+  const float4* st = stats + (int64_t)row * C;
   const int* cnt = counts + (int64_t)row * C;
-  const int64_t slot_row = (int64_t)row * C * cap;
+  const float* cx = cand_x + (int64_t)row * C * cap;
+  const int* ci = cand_i + (int64_t)row * C * cap;
 
-  if (t == 0) {
-    float M = -INFINITY;
-    for (int c = 0; c < C; ++c) M = fmaxf(M, st[c].x);
+  // Chunk metadata: prefix offsets of the candidate lists, lse and tau.
+  if (t < 64) {
+    float M = -INFINITY, tau = -INFINITY;
+    for (int c0 = 0; c0 < C; c0 += 64) {
+      const float4 v = c0 + lane < C ? st[c0 + lane] : make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
+      M = fmaxf(M, ddt::wave_reduce_uniform(v.x, ddt::OpMax()));
+      tau = fmaxf(tau, ddt::wave_reduce_uniform(v.z, ddt::OpMax()));
+    }
     float S = 0.f;
-    for (int c = 0; c < C; ++c) S += st[c].y * expf(st[c].x - M);
-    s_max = M;
-    s_lse = M + logf(S);
-    sh.out_count = 0u;
+    int carry = 0;
+    for (int c0 = 0; c0 < C; c0 += 64) {
+      const int c = c0 + lane;
+      const float4 v = c < C ? st[c] : make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
+      S += ddt::wave_reduce_uniform(c < C ? v.y * expf(v.x - M) : 0.f, ddt::OpSum());
+      int x = c < C ? cnt[c] : 0;
+      int incl = x;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      if (c < C) s.offs[c] = carry + incl - x;
+      carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) {
+      s.offs[C] = carry;
+      s.total = carry;
+      s.M = M;
+      s.tau = tau;
+      s.lse = M + logf(S);
+      s.nsurv = 0u;
+      s.nwin = 0u;
+      s.sh.out_count = 0u;
+    }
   }
   __syncthreads();
-  const float M = s_max;
+  const int total = s.total;
+  const float tau = s.tau;
 
-  // Visit every candidate of the row: f(x, token id).
-#define FOR_EACH_CAND(BODY)                                                   \
-  for (int c = 0; c < C; ++c) {                                               \
-    const int nc = cnt[c];                                                    \
-    for (int j = t; j < nc; j += kMergeThreads) {                             \
-      const float x = cand_x[slot_row + (int64_t)c * cap + j];                \
-      const int id = cand_i[slot_row + (int64_t)c * cap + j];                 \
-      BODY                                                                    \
-    }                                                                         \
+  // Survivors: candidates >= tau, loaded kLoadBatch per thread at a time.
+  for (int g0 = 0; g0 < total; g0 += kMergeThreads * kLoadBatch) {
+    float xv[kLoadBatch];
+    int iv[kLoadBatch];
+#pragma unroll
+    for (int r = 0; r < kLoadBatch; ++r) {
+      const int i = g0 + t + kMergeThreads * r;
+      xv[r] = -INFINITY;
+      iv[r] = -1;
+      if (i < total) {
+        int lo = 0, hi = C;  // last chunk with offs[c] <= i
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s.offs[mid] <= i) lo = mid; else hi = mid;
+        }
+        const int64_t at = (int64_t)lo * cap + (i - s.offs[lo]);
+        xv[r] = cx[at];
+        iv[r] = ci[at];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kLoadBatch; ++r) {
+      const bool keep = iv[r] >= 0 && xv[r] >= tau;
+      const uint64_t bm = ddt::ballot(keep);
+      uint32_t wb = 0u;
+      if (lane == 0 && bm) wb = atomicAdd(&s.nsurv, (uint32_t)__popcll(bm));
+      wb = (uint32_t)__builtin_amdgcn_readfirstlane((int)wb);
+      if (keep) {
+        const uint32_t pos = wb + ddt::lanes_below(bm);
+        if (pos < (uint32_t)kSurvCap) {
+          s.sx[pos] = xv[r];
+          s.si[pos] = iv[r];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int nsurv = (int)s.nsurv;
+  const float lse = s.lse;
+  float* out_lp = logp + (int64_t)row * K;
+  int32_t* out_tok = token + (int64_t)row * K;
+
+  if (nsurv <= kMergeThreads) {
+    // Rank every survivor among the survivors; ranks below K are outputs.
+    if (t < nsurv) {
+      const float xt = s.sx[t];
+      const int it = s.si[t];
+      int rank = 0;
+      for (int u = 0; u < nsurv; ++u) rank += beats(s.sx[u], s.si[u], xt, it);
+      if (rank < K) {
+        out_lp[rank] = xt - lse;
+        out_tok[rank] = it;
+      }
+    }
+    return;
   }
 
-  zero_hist(sh);
+  // More survivors than threads: exact radix select of the K largest, over
+  // the survivors in LDS when they fit, else over all candidates in global
+  // memory (only tie-heavy rows get there), then rank the K winners.
+  const bool in_lds = nsurv <= kSurvCap;
+  const int n_all = in_lds ? nsurv : total;
+  const float M = s.M;
+  auto elem_x = [&](int i) -> float {
+    if (in_lds) return s.sx[i];
+    int lo = 0, hi = C;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s.offs[mid] <= i) lo = mid; else hi = mid;
+    }
+    return cx[(int64_t)lo * cap + (i - s.offs[lo])];
+  };
+  auto elem_i = [&](int i) -> int {
+    if (in_lds) return s.si[i];
+    int lo = 0, hi = C;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s.offs[mid] <= i) lo = mid; else hi = mid;
+    }
+    return ci[(int64_t)lo * cap + (i - s.offs[lo])];
+  };
+  const int per = (n_all + kMergeThreads - 1) / kMergeThreads;
+
+  zero_hist(s.sh);
   __syncthreads();
-  FOR_EACH_CAND({ (void)id; atomicAdd(&sh.hist[rel_digit(M, x)], 1u); })
+  for (int r = 0; r < per; ++r) {
+    const int i = t + kMergeThreads * r;
+    if (i < n_all) atomicAdd(&s.sh.hist[rel_digit(M, elem_x(i))], 1u);
+  }
   __syncthreads();
-  find_digit(sh, (uint32_t)K);
-  const uint32_t d0 = sh.digit;
-  uint32_t need = sh.need;
-  const bool take_bin = need == sh.in_bin;
+  find_digit(s.sh, (uint32_t)K);
+  const uint32_t d0 = s.sh.digit;
+  const uint32_t need = s.sh.need;
+  const bool take_bin = need == s.sh.in_bin;
   uint32_t tkey = 0u, tik = 0u;
   const uint32_t idx_mask = idx_passes >= 4 ? 0xFFFFFFFFu : ((1u << (8 * idx_passes)) - 1u);
   if (!take_bin) {
-    uint32_t prefix = 0u, mask = 0u, inb = 0u;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      __syncthreads();
-      zero_hist(sh);
-      __syncthreads();
-      FOR_EACH_CAND({
-        (void)id;
-        if (rel_digit(M, x) == d0) {
-          const uint32_t k = ddt::f32_key(x);
-          if ((k & mask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
-        }
-      })
-      __syncthreads();
-      find_digit(sh, need);
-      prefix |= sh.digit << shift;
-      mask |= 255u << shift;
-      need = sh.need;
-      inb = sh.in_bin;
-    }
-    tkey = prefix;
-    if (need < inb) {
-      uint32_t ip = 0u, im = 0u;
-      for (int shift = 8 * (idx_passes - 1); shift >= 0; shift -= 8) {
-        __syncthreads();
-        zero_hist(sh);
-        __syncthreads();
-        FOR_EACH_CAND({
-          if (rel_digit(M, x) == d0 && ddt::f32_key(x) == tkey) {
-            const uint32_t ik = idx_mask - (uint32_t)id;
-            if ((ik & im) == ip) atomicAdd(&sh.hist[(ik >> shift) & 255u], 1u);
-          }
-        })
-        __syncthreads();
-        find_digit(sh, need);
-        ip |= sh.digit << shift;
-        im |= 255u << shift;
-        need = sh.need;
-      }
-      tik = ip;
-    }
+    refine_bucket(
+        s.sh, need, per, idx_passes,
+        [&](int r) {
+          const int i = t + kMergeThreads * r;
+          return i < n_all && rel_digit(M, elem_x(i)) == d0;
+        },
+        [&](int r) { return ddt::f32_key(elem_x(t + kMergeThreads * r)); },
+        [&](int r) { return idx_mask - (uint32_t)elem_i(t + kMergeThreads * r); }, tkey, tik);
   }
-  __syncthreads();
-  FOR_EACH_CAND({
+  for (int r = 0; r < per; ++r) {
+    const int i = t + kMergeThreads * r;
+    if (i >= n_all) continue;
+    const float x = elem_x(i);
     const uint32_t d = rel_digit(M, x);
     bool sel = d > d0;
     if (d == d0) {
@@ -325,28 +439,25 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
         sel = true;
       } else {
         const uint32_t k = ddt::f32_key(x);
-        sel = k > tkey || (k == tkey && (idx_mask - (uint32_t)id) >= tik);
+        sel = k > tkey || (k == tkey && (idx_mask - (uint32_t)elem_i(i)) >= tik);
       }
     }
     if (sel) {
-      const uint32_t pos = atomicAdd(&sh.out_count, 1u);
-      wx[pos] = x;
-      wi[pos] = id;
+      const uint32_t pos = atomicAdd(&s.nwin, 1u);
+      if (pos < (uint32_t)DDTREE_MAX_K) {
+        s.wx[pos] = x;
+        s.wi[pos] = elem_i(i);
+      }
     }
-  })
-#undef FOR_EACH_CAND
+  }
   __syncthreads();
-  // Rank the K winners: larger logit first, then smaller id.
   if (t < K) {
-    const float xt = wx[t];
-    const int it = wi[t];
+    const float xt = s.wx[t];
+    const int it = s.wi[t];
     int rank = 0;
-    for (int u = 0; u < K; ++u) {
-      const float xu = wx[u];
-      rank += (xu > xt) || (xu == xt && wi[u] < it);
-    }
-    logp[(int64_t)row * K + rank] = xt - s_lse;
-    token[(int64_t)row * K + rank] = it;
+    for (int u = 0; u < K; ++u) rank += beats(s.wx[u], s.wi[u], xt, it);
+    out_lp[rank] = xt - lse;
+    out_tok[rank] = it;
   }
 }
 
@@ -365,7 +476,7 @@ TopkPlan topk_plan(int L, int V, int K) {
   p.idx_passes = (bits + 7) / 8;
   const size_t LC = (size_t)L * p.C;
   p.stats_off = 0;
-  p.counts_off = align_up(p.stats_off + LC * sizeof(float2), 256);
+  p.counts_off = align_up(p.stats_off + LC * sizeof(float4), 256);
   p.candx_off = align_up(p.counts_off + LC * sizeof(int), 256);
   p.candi_off = align_up(p.candx_off + LC * p.cap * sizeof(float), 256);
   p.bytes = align_up(p.candi_off + LC * p.cap * sizeof(int), 256);
@@ -375,8 +486,9 @@ TopkPlan topk_plan(int L, int V, int K) {
 int topk_launch(const float* logits, int64_t stride, int L, int V, int K,
                 float* logp, int32_t* token, void* ws, hipStream_t stream) {
   const TopkPlan p = topk_plan(L, V, K);
+  if (p.C > kMergeThreads) return DDTREE_ERR_UNSUPPORTED;
   char* w = static_cast<char*>(ws);
-  float2* stats = reinterpret_cast<float2*>(w + p.stats_off);
+  float4* stats = reinterpret_cast<float4*>(w + p.stats_off);
   int* counts = reinterpret_cast<int*>(w + p.counts_off);
   float* cx = reinterpret_cast<float*>(w + p.candx_off);
   int* ci = reinterpret_cast<int*>(w + p.candi_off);

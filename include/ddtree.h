@@ -58,6 +58,7 @@ typedef enum ddtree_status {
 #define DDTREE_MAX_K 1024      /* top-K kept per position                    */
 #define DDTREE_MAX_B 1024      /* node budget (the pages sweep 16..1024)     */
 #define DDTREE_MAX_LK 32768    /* L * K: the whole top-K table sits in LDS   */
+#define DDTREE_MAX_V 4194304   /* vocabulary (1024 chunks of 4096 logits)    */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* ddtree_status_string(int status);
@@ -75,7 +76,8 @@ int ddtree_version(void);
  * logits      fp32 [L, row_stride]; row i holds V logits of block position i
  *             (0-based). Values must be finite.
  * row_stride  elements between rows, >= V.
- * L, V, K     1 <= L <= DDTREE_MAX_L, 1 <= K <= min(V, DDTREE_MAX_K).
+ * L, V, K     1 <= L <= DDTREE_MAX_L, 1 <= V <= DDTREE_MAX_V,
+ *             1 <= K <= min(V, DDTREE_MAX_K).
  * logp        out fp32 [L, K]: log q_i of the selected tokens, rank order.
  * token       out int32 [L, K]: their token ids.
  * ws/ws_bytes device scratch of at least ddtree_topk_workspace_bytes().
