@@ -3,43 +3,54 @@
 // ancestors and itself; section 10: grouped-query attention).
 //
 // Decomposition. For kv-head g the query rows are rho = n * G + i (node n,
-// i-th query head of the group); all N * G rows share the same keys, so one
-// K/V tile staged in LDS feeds 128 query rows (4 waves x 32). The key range
-// [0, S + N) (prefix, then the tree block) is cut into 64-key blocks and the
-// blocks into `splits` contiguous ranges. Prefix blocks are dense; only
-// blocks reaching past S read the mask.
+// i-th query head of the group); all N * G rows share the same keys. A
+// workgroup owns a tile of 64 query rows (two waves of 32 rows) and a range
+// of keys, and runs four key streams side by side: the range is cut into
+// 128-key superblocks, and stream s computes the 32-key block s of every
+// superblock. So a workgroup is 8 waves (2 row waves x 4 streams), two per
+// SIMD: while one wave of a SIMD runs its softmax the other keeps the
+// matrix core busy. After the loop the four streams' partial results are
+// merged through LDS. Blocks before S are dense prefix keys; only blocks
+// reaching past S read the ancestor mask.
+//
+// Splits. The key range [0, S + N) is cut into `splits` runs of superblocks
+// so that the grid about fills the chip with one workgroup per CU (LDS
+// allows one). Splits > 1 write unnormalised partial outputs with their
+// reference maximum and sum (base-2 domain) to the workspace, in the
+// accumulator's register layout so that every store and load is 1 KB
+// contiguous; a combine kernel merges them.
 //
 // Grid mapping. Workgroups are dealt to the 8 XCDs round-robin by id, and
-// each XCD has its own L2. Ids are decoded so that all row tiles of one
-// (kv-head, split) land on the same XCD: the K/V range they share is then
-// fetched from HBM once and re-read from that XCD's L2.
+// each XCD has its own L2. Ids are decoded so that each XCD receives a
+// contiguous run of the (kv-head, split, tile) order: the tiles sharing a
+// key range then sit on one XCD, which fetches those K/V rows from HBM once
+// and serves the other tiles from its L2.
 //
-// Data movement. K and V tiles go from global memory straight into LDS
+// Data movement. K and V blocks go from global memory straight into LDS
 // (global_load_lds, 16 bytes per lane, no registers), double-buffered: the
-// copy of block b + 1 is in flight while block b is computed. A wave's copy
-// lands 1 KB contiguously (lane l at +16 l), and each lane fetches whichever
-// 16-byte chunk belongs at its slot. K rows are row-major with the chunk
-// index XOR-ed by the row (slot = chunk ^ fk(row)), so the 32 rows a K
-// operand read touches fall in different banks. V is kept chunk-major inside
-// groups of 1 KB (4 keys at D = 128, 8 at D = 64): slot = chunk * rows +
-// row, so the 8 keys a transposing read touches sit side by side and every
-// operand address is a per-lane base plus compile-time offsets.
+// copy of superblock i + 1 is in flight while superblock i is computed. A
+// wave's copy lands 1 KB contiguously (lane l at +16 l), and each lane
+// fetches whichever 16-byte chunk belongs at its slot. K and V rows are
+// row-major with the chunk index XOR-ed by a function of the row (slot =
+// chunk ^ f(row)): for K the 32 rows an operand read touches, for V the 4
+// keys x 4 chunks a transposing read touches fall in different banks. The
+// XOR only permutes chunks inside aligned groups of four, so every four
+// lanes of a copy still fetch one contiguous 64-byte piece (a copy whose
+// lanes jump between rows runs at a third of the speed).
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16, wave64). Each wave computes
 // S^T = K Q^T for its 32 query columns: A = 32 keys x 16 dims of K (one
 // 16-byte LDS read per lane), B = Q^T held in registers for the whole
 // kernel. In the 32x32 accumulator, lane (j, h) = (lane & 31, lane >> 5)
 // owns query column j and key rows 8*(r/4) + 4*h + r%4 of register r, so
-// the online softmax is lane-local except one exchange with lane ^ 32.
-// Rounded to bf16, those registers are the B operand of O^T = V^T P^T when
-// each 16-key step takes keys {4h..4h+3} then {8+4h..8+4h+3} on lane half h.
-// The matching V^T A operand comes from row-major V by two transposing LDS
-// reads (ds_read_b64_tr_b16): within each 16-lane group, lane i receives
-// element i%4 of the 4-element reads of lanes 4e + i/4, so lanes point at
-// (key 4h + e, dims 4*(lane%4) + 16*((lane/16)%2)) and get 4 keys of one dim.
-//
-// Splits > 1 write unnormalised partial outputs with their running max and
-// sum (base-2 domain) to the workspace; a combine kernel merges them.
+// the online softmax is lane-local except one exchange between the lane
+// halves (v_permlane32_swap). Rounded to bf16, those registers are the B
+// operand of O^T = V^T P^T when each 16-key step takes keys {4h..4h+3} then
+// {8+4h..8+4h+3} on lane half h. The matching V^T A operand comes from V by
+// two transposing LDS reads (ds_read_b64_tr_b16): within each 16-lane
+// group, lane i receives element i%4 of the 4-element reads of lanes
+// 4e + i/4, so lanes point at (key 4h + e, dims 4*(lane%4) +
+// 16*((lane/16)%2)) and get 4 keys of one dim.
 #include <cstdlib>
 
 #include "common.hpp"
@@ -52,22 +63,26 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-constexpr int kBK = 64;        // keys per block
-constexpr int kWaves = 4;
+constexpr int kBK = 32;                       // keys per block (one stream's step)
+constexpr int kStreams = 4;                   // key streams per workgroup
+constexpr int kRowWaves = 2;                  // 32-row query waves per workgroup
+constexpr int kWaves = kStreams * kRowWaves;  // 8: two per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerTile = 32 * kWaves;
+constexpr int kRowsPerTile = 32 * kRowWaves;
+constexpr int kSBK = kBK * kStreams;          // keys per superblock
 constexpr int kXcds = 8;
 
 template <int D>
 struct Cfg {
-  static constexpr int KS = D / 16;              // MFMA k-steps for Q.K
-  static constexpr int DT = D / 32;              // 32-wide output tiles of P.V
-  static constexpr int NS = D / 8;               // 16-byte slots per row
-  static constexpr int ROWB = 2 * D;             // bytes per row
-  static constexpr int TILEB = kBK * ROWB;       // bytes per K or V tile
-  static constexpr int ROWS_PER_COPY = 1024 / ROWB;         // rows per 1 KB wave copy
-  static constexpr int COPIES = TILEB / 1024 / kWaves;      // copies per wave per tile
-  static constexpr int VG = ROWS_PER_COPY;                  // keys per chunk-major V group
+  static constexpr int KS = D / 16;                          // MFMA k-steps for Q.K
+  static constexpr int DT = D / 32;                          // 32-wide output tiles of P.V
+  static constexpr int NS = D / 8;                           // 16-byte slots per row
+  static constexpr int ROWB = 2 * D;                         // bytes per row
+  static constexpr int TILEB = kBK * ROWB;                   // bytes per K or V block
+  static constexpr int ROWS_PER_COPY = 1024 / ROWB;          // rows per 1 KB wave copy
+  static constexpr int COPIES = TILEB / 1024 / kRowWaves;    // copies per wave per block
+  static constexpr int STAGEB = kStreams * TILEB;            // one operand of a superblock
+  static constexpr int OB = 64 * DT * 16 * 4;                // one wave's fp32 output tile
 };
 
 // K rows are read 32 at a time at one chunk: spread consecutive rows over
@@ -77,33 +92,93 @@ __device__ __forceinline__ int fk(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
 
+// V is read 4 consecutive keys x 4 chunks at a time (per 32 lanes): give
+// the 4 keys disjoint sets of 16-byte bank slots.
+template <int D>
+__device__ __forceinline__ int fv(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
 
-// Copy the 64-key block starting at key0 of K and V into the tile buffers.
-// Rows past the last key (KT - 1) are clamped to it: they are real, finite
-// data whose scores are masked and whose weights are exactly 0.
+// v_permlane32_swap of a value with itself leaves the low half's values in
+// one result and the high half's in the other, on every lane: their max is
+// the max over lanes j and j + 32.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Per-lane source offsets of a wave's copies, fixed for the whole kernel:
+// copy i of row wave rw fetches rows 4 (rw * COPIES + i) + lane / NS (D =
+// 128), each lane the chunk that belongs at its 16-byte slot.
+// (fv(row) depends only on the row modulo 4, i.e. on the lane, so the V
+// offsets of the copies differ by whole rows.)
 template <int D>
-__device__ __forceinline__ void copy_block(const uint16_t* kh, const uint16_t* vh, int key0, int KT,
-                                           char* kt_lds, char* vt_lds, int wave, int lane) {
+struct CopyLanes {
+  uint32_t kb[Cfg<D>::COPIES];  // byte offsets from the block's row 0
+  uint32_t vb;                  // V offset of copy 0; copy i adds i rows per copy
+};
+template <int D>
+__device__ __forceinline__ int copy_row(int rw, int i, int lane) {
   using C = Cfg<D>;
-  const int last = KT - 1;
-  const int kslot = lane % C::NS;             // K: row-major, XOR-swizzled
-  const int vchunk = lane / C::VG;            // V: chunk-major inside a group
-  const int vrow = lane % C::VG;
+  return (rw * C::COPIES + i) * C::ROWS_PER_COPY + lane / C::NS;
+}
+template <int D>
+__device__ __forceinline__ CopyLanes<D> copy_lanes(int rw, int lane) {
+  using C = Cfg<D>;
+  static_assert(C::ROWS_PER_COPY % 4 == 0, "fv is periodic in 4 rows");
+  CopyLanes<D> cl;
+  const int slot = lane % C::NS;
 #pragma unroll
   for (int i = 0; i < C::COPIES; ++i) {
-    const int copy = wave * C::COPIES + i;
-    const int krow = copy * C::ROWS_PER_COPY + lane / C::NS;
-    const int kkey = min(key0 + krow, last);
-    const int vkey = min(key0 + copy * C::VG + vrow, last);
-    const uint16_t* ksrc = kh + (uint32_t)(kkey * D + 8 * (kslot ^ fk<D>(krow)));
-    const uint16_t* vsrc = vh + (uint32_t)(vkey * D + 8 * vchunk);
-    __builtin_amdgcn_global_load_lds(ksrc, (lds_void_t*)(kt_lds + copy * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vsrc, (lds_void_t*)(vt_lds + copy * 1024), 16, 0, 0);
+    const int row = copy_row<D>(rw, i, lane);
+    cl.kb[i] = (uint32_t)(row * C::ROWB + 16 * (slot ^ fk<D>(row)));
+  }
+  const int row0 = copy_row<D>(rw, 0, lane);
+  cl.vb = (uint32_t)(row0 * C::ROWB + 16 * (slot ^ fv<D>(row0)));
+  return cl;
+}
+
+// Copy the 32-key block starting at key0 of K or V into LDS; the two row
+// waves of a stream split the copies. Source = block base (uniform, scalar
+// registers) + the lane's fixed offset. In the last block rows past the
+// last key (KT - 1) are clamped to it: they are real, finite data whose
+// scores are masked and whose weights are exactly 0.
+template <int D, bool IS_V>
+__device__ __forceinline__ void copy_block(const uint16_t* src, int key0, int KT, char* dst_lds,
+                                           int rw, const CopyLanes<D>& cl) {
+  using C = Cfg<D>;
+  const char* base = reinterpret_cast<const char*>(src + (int64_t)key0 * D);
+  const int lane = threadIdx.x & 63;
+  auto off = [&](int i) -> uint32_t {
+    return IS_V ? cl.vb + (uint32_t)(i * C::ROWS_PER_COPY * C::ROWB) : cl.kb[i];
+  };
+  if (key0 + kBK <= KT) {
+#pragma unroll
+    for (int i = 0; i < C::COPIES; ++i) {
+      const int copy = rw * C::COPIES + i;
+      __builtin_amdgcn_global_load_lds(base + off(i), (lds_void_t*)(dst_lds + copy * 1024), 16,
+                                       0, 0);
+    }
+  } else {
+    // Rows clamped to key KT - 1 (the block may lie wholly past it): a
+    // per-lane address from the clamped key, plus the chunk's byte offset
+    // within its row (never negative).
+#pragma unroll
+    for (int i = 0; i < C::COPIES; ++i) {
+      const int copy = rw * C::COPIES + i;
+      const int row = copy_row<D>(rw, i, lane);
+      const int key = min(key0 + row, KT - 1);
+      const char* p = reinterpret_cast<const char*>(src + (int64_t)key * D) +
+                      (off(i) - (uint32_t)(row * C::ROWB));
+      __builtin_amdgcn_global_load_lds(p, (lds_void_t*)(dst_lds + copy * 1024), 16, 0, 0);
+    }
   }
 }
 
@@ -113,83 +188,183 @@ __device__ __forceinline__ void copy_block(const uint16_t* kh, const uint16_t* v
 // same softmax because numerator and denominator share the stale maximum.
 constexpr float kRescaleSlack = 8.0f;
 
-// One 64-key block for this wave's 32 query columns: S^T = K Q^T, online
-// softmax, O^T += V^T P^T. Blocks reaching past S hold tree keys: there a
-// key S + m is visible to the lane's node only if bit m of its ancestor row
-// is set (prefix keys are always visible). The mask is applied by a
-// wave-uniform branch that touches only the scores, so the output
-// accumulators follow a single path through the loop.
+// Visibility of the 32 keys key0..key0+31 of a block reaching past S, for
+// one node: bit t is set iff key key0 + t is visible. Prefix keys are always
+// visible; tree key S + m is visible iff bit m of the node's ancestor row is
+// set; keys from S + N on do not exist (a block may lie wholly past them).
+// mw0, mw1 are the row's words max(key0 - S, 0) / 32 and the next one.
+__device__ __forceinline__ uint32_t block_visibility(int key0, int S, int N, uint32_t mw0,
+                                                     uint32_t mw1) {
+  const int t0 = key0 - S;  // tree index of the block's first key, > -32
+  uint32_t vis = t0 >= 0 ? __builtin_amdgcn_alignbit(mw1, mw0, (uint32_t)(t0 & 31))
+                         : (mw0 << (-t0)) | ((1u << (-t0)) - 1u);
+  const int lim = S + N - key0;  // keys of the block that exist
+  if (lim < 32) vis &= lim > 0 ? (1u << lim) - 1u : 0u;
+  return vis;
+}
+
+// Per-lane offsets of the V^T operand reads. Pointer lane l covers key
+// 16 mm + 8 half + 4 h + e (e = (l & 15) >> 2) and dims 32 dt + 16 ((l >> 4)
+// & 1) + 4 (l & 3), i.e. chunk 4 dt + c0. Since 16 mm + 8 half + 4 h is a
+// multiple of 4, the row's swizzle fv is the lane's own constant fv(e), so
+// each dt has a per-lane offset and mm, half add compile-time row offsets.
+// The offsets are made opaque so each read is one pointer step from its
+// array: the LDS alias analysis follows only a few levels of address
+// arithmetic (and the optimiser would split a sum into one level per term);
+// a read it cannot attribute to its array has to wait for every copy in
+// flight.
 template <int D>
-__device__ __forceinline__ void block_step(const char* Kb, const char* Vb,
-                                           const bf16x8 (&qf)[Cfg<D>::KS],
-                                           f32x16 (&o)[Cfg<D>::DT], float& m_run, float& l_run,
-                                           float scale_log2, int lane, int key0, int S, int N,
-                                           int wlo, uint32_t mw0, uint32_t mw1, uint32_t mw2) {
+struct VLanes {
+  int off[Cfg<D>::DT];
+};
+template <int D>
+__device__ __forceinline__ VLanes<D> v_lanes(int lane) {
   using C = Cfg<D>;
+  const int h = lane >> 5, e4 = (lane & 15) >> 2;
+  const int c0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  VLanes<D> vl;
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+    vl.off[dt] = (4 * h + e4) * C::ROWB + 16 * ((4 * dt + c0) ^ fv<D>(e4)) + 8 * (lane & 1);
+    asm("" : "+v"(vl.off[dt]));
+  }
+  return vl;
+}
+
+// The softmax weights of one 32-key block as the B operands of its two
+// 16-key P.V steps (bf16).
+struct PBlock {
+  bf16x8 p[2];
+};
+
+// V^T operands of one 32-key block: [mm][dt], two transposing reads each.
+template <int D>
+__device__ __forceinline__ void read_v(const char* Vb, const VLanes<D>& vl,
+                                       bf16x8 (&va)[2][Cfg<D>::DT]) {
+  using C = Cfg<D>;
+  constexpr int kMM = 16 * C::ROWB;   // offset per 16 keys
+  constexpr int kHalf = 8 * C::ROWB;  // offset of keys +8
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const char* p0 = Vb + vl.off[dt] + mm * kMM;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0 + kHalf));
+      va[mm][dt] = __builtin_bit_cast(
+          bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                               hi[0], hi[1], hi[2], hi[3]});
+    }
+}
+
+__device__ __forceinline__ bf16x8 bf16_ones() {
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  return ones;
+}
+
+// O^T += V^T P^T for one block, and the row sums of its bf16 weights on the
+// matrix core (A = all ones): the denominator sums exactly the weights the
+// numerator uses.
+template <int D>
+__device__ __forceinline__ void block_pv(const char* Vb, const VLanes<D>& vl, const PBlock& pb,
+                                         f32x16 (&o)[Cfg<D>::DT], f32x16& lsum) {
+  using C = Cfg<D>;
+  bf16x8 va[2][C::DT];
+  read_v<D>(Vb, vl, va);
+  const bf16x8 ones = bf16_ones();
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm) {
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mm][dt], pb.p[mm], o[dt], 0, 0, 0);
+    lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb.p[mm], lsum, 0, 0, 0);
+  }
+}
+
+// S^T = K Q^T for this wave's 32 query columns over one 32-key block, and,
+// when `pv`, the P.V products of the previous block at the same time: the
+// dependent chain of Q.K products and the independent P.V products
+// alternate on the matrix core, and the softmax of this block (vector ALU)
+// can then run while the last of them finish.
+template <int D>
+__device__ __forceinline__ f32x16 block_qk_pv(const char* Kb, const char* Vb, bool pv,
+                                              const bf16x8 (&qf)[Cfg<D>::KS], const PBlock& pb,
+                                              const VLanes<D>& vl, f32x16 (&o)[Cfg<D>::DT],
+                                              f32x16& lsum, int lane) {
+  using C = Cfg<D>;
+  static_assert(C::KS == 2 * C::DT, "one P.V product per Q.K step");
   const int j = lane & 31, h = lane >> 5;
-  const bool masked = key0 + kBK > S;
-  // S^T = K Q^T as two independent accumulator chains (keys 0-31 and
-  // 32-63) interleaved step by step, with the K operand reads kept a few
-  // steps ahead so LDS latency hides behind the MFMAs.
-  f32x16 sacc[2];
+  const char* krow = Kb + j * C::ROWB;
+  const int f = fk<D>(j);
+  bf16x8 ka[C::KS];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+  for (int ks = 0; ks < C::KS; ++ks)
+    ka[ks] = *reinterpret_cast<const bf16x8*>(krow + 16 * ((2 * ks + h) ^ f));
+  f32x16 sacc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-  {
-    const char* krow0 = Kb + j * C::ROWB;
-    const int f = fk<D>(j);  // the same for rows j and 32 + j
-    constexpr int NSTEP = 2 * C::KS;
-    constexpr int AHEAD = 4;
-    bf16x8 ka[NSTEP];
+  for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+  if (pv) {
+    bf16x8 va[2][C::DT];
+    read_v<D>(Vb, vl, va);
 #pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
-      const int ks = i >> 1, kt = i & 1;
-      ka[i] = *reinterpret_cast<const bf16x8*>(krow0 + kt * 32 * C::ROWB + 16 * ((2 * ks + h) ^ f));
+    for (int ks = 0; ks < C::KS; ++ks) {
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sacc, 0, 0, 0);
+      const int mm = ks / C::DT, dt = ks % C::DT;
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mm][dt], pb.p[mm], o[dt], 0, 0, 0);
     }
+    const bf16x8 ones = bf16_ones();
+    lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb.p[0], lsum, 0, 0, 0);
+    lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb.p[1], lsum, 0, 0, 0);
+    // Schedule: the reads of two steps ahead (one K read and two V reads per
+    // step), then per step its two products and the next step's reads; this
+    // keeps few operands live at once.
+    constexpr int AH = 2;
+    __builtin_amdgcn_sched_group_barrier(0x100, 3 * AH, 0);
 #pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
-      const int ks = i >> 1, kt = i & 1;
-      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[ks], sacc[kt], 0, 0, 0);
+    for (int i = 0; i < C::KS - AH; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
     }
-    // Schedule: AHEAD reads, then alternate one MFMA with one read.
-    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * AH + 2, 0);
+  } else {
 #pragma unroll
-    for (int i = 0; i < NSTEP - AHEAD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+    for (int ks = 0; ks < C::KS; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sacc, 0, 0, 0);
   }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[kt][r] *= scale_log2;
+  return sacc;
+}
+
+// Online softmax of one block's scores (unscaled until the exponent, where
+// scale * log2(e) and the reference maximum enter as one fma). For blocks
+// reaching past S, `vis` (block_visibility) masks the scores by a
+// wave-uniform branch that touches only the scores. Rescaling multiplies
+// the running output and sums, so it must come after the previous block's
+// P.V products are issued (the hardware orders the two).
+template <int D>
+__device__ __forceinline__ PBlock block_softmax(f32x16 sacc, f32x16 (&o)[Cfg<D>::DT],
+                                                float& m_run, f32x16& lsum, float c, int lane,
+                                                bool masked, uint32_t vis) {
+  using C = Cfg<D>;
+  const int h = lane >> 5;
   if (masked) {
+    const uint32_t vh = vis >> (4 * h);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tn = key0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3) - S;
-        const int wi = (tn >> 5) - wlo;
-        const uint32_t word = wi == 0 ? mw0 : (wi == 1 ? mw1 : mw2);
-        const uint32_t vis = (uint32_t)(tn < 0) | ((uint32_t)(tn < N) & (word >> (tn & 31)));
-        sacc[kt][r] = (vis & 1u) ? sacc[kt][r] : -INFINITY;
-      }
+    for (int r = 0; r < 16; ++r)
+      if (!((vh >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[r] = -INFINITY;
   }
-  float bmax = -INFINITY;
+  float bm = sacc[0];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, sacc[kt][r]);
-  bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+  for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[r]);
+  const float bmax = halves_max(bm) * c;  // c > 0: the scaled maximum
   // Lazy rescale: move the reference maximum only when some column needs it.
   const bool grow = bmax > m_run + kRescaleSlack;
   if (__builtin_amdgcn_ballot_w64(grow)) {
     const float m_new = fmaxf(m_run, bmax);
     const float corr = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
-    l_run *= corr;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lsum[r] *= corr;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -198,48 +373,12 @@ __device__ __forceinline__ void block_step(const char* Kb, const char* Vb,
   }
   // A column that has seen no visible key yet keeps m_run = -inf; use 0 as
   // its reference so that masked weights come out as exp2(-inf) = 0.
-  const float m_use = m_run == -INFINITY ? 0.f : m_run;
-  float psum = 0.f;
+  const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+  PBlock pb;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(sacc[kt][r] - m_use);
-      sacc[kt][r] = p;
-      psum += p;
-    }
-  l_run += psum;
-
-  // V^T operands from two transposing reads per 16 keys. Pointer lane l
-  // covers key 16 mm + 8 half + 4 h + e (e = (l & 15) >> 2) and dims
-  // 32 dt + 16 ((l >> 4) & 1) + 4 (l & 3); in the chunk-major V layout that
-  // is a per-lane base plus offsets fixed at compile time.
-  const int e4 = (lane & 15) >> 2;
-  const int c0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const char* vbase =
-      D == 128 ? Vb + h * 1024 + (c0 * 4 + e4) * 16 + 8 * (lane & 1)
-               : Vb + (c0 * 8 + 4 * h + e4) * 16 + 8 * (lane & 1);
-  constexpr int kMM = D == 128 ? 4096 : 2048;   // offset per 16 keys
-  constexpr int kHalf = D == 128 ? 2048 : 1024; // offset of keys +8
-  constexpr int kDT = D == 128 ? 256 : 512;     // offset per 32 dims
-#pragma unroll
-  for (int mm = 0; mm < 4; ++mm) {
-    bf16x8 bp;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bp[e] = (__bf16)sacc[mm >> 1][8 * (mm & 1) + e];
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const char* p0 = vbase + mm * kMM + dt * kDT;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0 + kHalf));
-      const bf16x8 a = __builtin_bit_cast(
-          bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
-                                                               hi[0], hi[1], hi[2], hi[3]});
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, o[dt], 0, 0, 0);
-    }
-    // At most one 16-key step of V operands in flight (register budget).
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  for (int r = 0; r < 16; ++r)
+    pb.p[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[r], c, neg_m));
+  return pb;
 }
 
 template <int D>
@@ -248,64 +387,75 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t* __restrict__ v, int S, int S_cap, int N, int Hq, int Hkv,
     float scale_log2, const uint32_t* __restrict__ anc, int W,
     uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int tiles, int splits, int blocks_per_split, int rows_pad, int xcd_map) {
+    int tiles, int splits, int sb_per_split, int wgs, int per_xcd) {
   using C = Cfg<D>;
-  // Two buffers per operand, as distinct arrays: every read and every copy
+  // Two stages per operand, as distinct arrays: every read and every copy
   // below names a fixed array, so the compiler can tell that reading one
-  // buffer never has to wait for the copy in flight into the other.
-  __shared__ __attribute__((aligned(1024))) char k0[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char v0[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char k1[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char v1[C::TILEB];
+  // stage never has to wait for the copy in flight into the other. Stream s
+  // owns bytes [s * TILEB, (s + 1) * TILEB) of each.
+  __shared__ __attribute__((aligned(1024))) char k0[C::STAGEB];
+  __shared__ __attribute__((aligned(1024))) char v0[C::STAGEB];
+  __shared__ __attribute__((aligned(1024))) char k1[C::STAGEB];
+  __shared__ __attribute__((aligned(1024))) char v1[C::STAGEB];
+  __shared__ float2 mlx[kWaves * 64];
 
-  int tile, g, split;
-  {
-    const int bid = blockIdx.x;
-    int grp;
-    if (xcd_map) {
-      const int local = bid / kXcds;
-      grp = (local / tiles) * kXcds + bid % kXcds;
-      tile = local % tiles;
-    } else {
-      grp = bid / tiles;
-      tile = bid % tiles;
-    }
-    g = grp / splits;
-    split = grp % splits;
-  }
+  // Workgroup id -> position in the (kv-head, split, tile) order, one
+  // contiguous run per XCD. Ids past the work exit before any barrier.
+  const int idx = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (idx >= wgs) return;
+  const int tile = idx % tiles;
+  const int gs = idx / tiles;
+  const int split = gs % splits, g = gs / splits;
+
   const int G = Hq / Hkv, R = N * G;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // The wave index is uniform: keep it (and all that derives from it, such
+  // as the LDS destinations of the copies) in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int st = wave >> 1, rw = wave & 1;
   const int j = lane & 31, h = lane >> 5;
-  const int rho = tile * kRowsPerTile + wave * 32 + j;
+  const int row0 = tile * kRowsPerTile + rw * 32;
+  const bool live = row0 < R;  // wave-uniform: the wave has query rows
+  const int rho = row0 + j;
   const bool row_ok = rho < R;
   const int node = row_ok ? rho / G : 0;
   const int hq = g * G + (row_ok ? rho % G : 0);
 
   const int KT = S + N;
-  const int NB = (KT + kBK - 1) / kBK;
-  const int b0 = split * blocks_per_split;
-  const int b1 = min(NB, b0 + blocks_per_split);
+  const int NSB = (KT + kSBK - 1) / kSBK;
+  const int sb0 = split * sb_per_split;
+  const int sb1 = min(NSB, sb0 + sb_per_split);
   const uint16_t* kh = k + (int64_t)g * S_cap * D;
   const uint16_t* vh = v + (int64_t)g * S_cap * D;
   const uint32_t* arow = anc + (int64_t)node * W;
+  const int soff = st * C::TILEB;
 
-  // Mask words of a block (the at most 3 words of this lane's node that
-  // cover its tree keys) are loaded one block ahead, before that block's
-  // copy, so they have always arrived when the block is computed and no wait
-  // for them can stall on an in-flight copy.
-  int wlo_n = 0;
-  uint32_t mw0_n = 0u, mw1_n = 0u, mw2_n = 0u;
+  // The two mask words of a block are loaded one superblock ahead, before
+  // that superblock's copy, so they have always arrived when the block is
+  // computed and no wait for them can stall on an in-flight copy.
+  uint32_t mw0_n = 0u, mw1_n = 0u;
   auto fetch_mask = [&](int key0) {
-    wlo_n = max(0, key0 - S) >> 5;
-    mw0_n = mw1_n = mw2_n = 0u;
-    if (key0 + kBK > S && row_ok) {
-      mw0_n = wlo_n < W ? arow[wlo_n] : 0u;
-      mw1_n = wlo_n + 1 < W ? arow[wlo_n + 1] : 0u;
-      mw2_n = wlo_n + 2 < W ? arow[wlo_n + 2] : 0u;
+    mw0_n = mw1_n = 0u;
+    if (key0 + kBK > S && key0 < KT && row_ok) {
+      const int wlo = max(0, key0 - S) >> 5;
+      mw0_n = wlo < W ? arow[wlo] : 0u;
+      mw1_n = wlo + 1 < W ? arow[wlo + 1] : 0u;
     }
   };
-  fetch_mask(b0 * kBK);
-  copy_block<D>(kh, vh, b0 * kBK, KT, k0, v0, wave, lane);
+  const CopyLanes<D> cl = copy_lanes<D>(rw, lane);
+  // Blocks wholly past the last key are still copied (every row clamped to
+  // the last key) and computed (every key masked): every wave then runs one
+  // straight path, and no stage ever holds data that is not a finite K or V
+  // row.
+  auto copy_k = [&](int sb, char* dst) {
+    copy_block<D, false>(kh, (sb * kStreams + st) * kBK, KT, dst + soff, rw, cl);
+  };
+  auto copy_v = [&](int sb, char* dst) {
+    copy_block<D, true>(vh, (sb * kStreams + st) * kBK, KT, dst + soff, rw, cl);
+  };
+  const VLanes<D> vl = v_lanes<D>(lane);
+  fetch_mask((sb0 * kStreams + st) * kBK);
+  copy_k(sb0, k0);
 
   bf16x8 qf[C::KS];
   {
@@ -326,124 +476,196 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;
+  f32x16 lsum;  // every register holds the running sum of the lane's column
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lsum[r] = 0.f;
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // One step: compute block b from (kb, vb) while block b + 1 is copied into
-  // (kn, vn); the loop below alternates the buffers, unrolled by two.
-  auto step = [&](int b, const char* kb, const char* vb, char* kn, char* vn) {
-    const int wlo = wlo_n;
-    const uint32_t mw0 = mw0_n, mw1 = mw1_n, mw2 = mw2_n;
-    if (b + 1 < b1) {
-      fetch_mask((b + 1) * kBK);
-      copy_block<D>(kh, vh, (b + 1) * kBK, KT, kn, vn, wave, lane);
+  // Software pipeline over superblocks. Step i forms the scores of block i
+  // and its softmax weights, and issues the P.V products of block i - 1
+  // together with the Q.K products of block i. So the V rows of block i are
+  // first read in step i + 1: step i copies K of superblock i + 1 and V of
+  // superblock i, each into the stage the step before last finished with
+  // (K: i + 1 mod 2; V: i mod 2). The first step (no P.V) and the last P.V
+  // are peeled; the loop is unrolled by two so every access names a fixed
+  // array.
+  PBlock pb;  // weights of the previous block
+  auto vis_of = [&](int key0, uint32_t mw0, uint32_t mw1) {
+    return key0 + kBK > S ? block_visibility(key0, S, N, mw0, mw1) : ~0u;
+  };
+  auto step = [&](int sb, bool first, const char* kc, char* kn, char* vdst, const char* vprev) {
+    const uint32_t mw0 = mw0_n, mw1 = mw1_n;
+    if (sb + 1 < sb1) {
+      fetch_mask(((sb + 1) * kStreams + st) * kBK);
+      copy_k(sb + 1, kn);
     }
-    block_step<D>(kb, vb, qf, o, m_run, l_run, scale_log2, lane, b * kBK, S, N, wlo, mw0, mw1,
-                  mw2);
+    copy_v(sb, vdst);
+    const int key0 = (sb * kStreams + st) * kBK;
+    const f32x16 sacc =
+        block_qk_pv<D>(kc + soff, vprev + soff, !first, qf, pb, vl, o, lsum, lane);
+    pb = block_softmax<D>(sacc, o, m_run, lsum, scale_log2, lane, key0 + kBK > S,
+                          vis_of(key0, mw0, mw1));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
+  step(sb0, true, k0, k1, v0, v1);
 #pragma unroll 1
-  for (int b = b0; b < b1; b += 2) {
-    step(b, k0, v0, k1, v1);
-    if (b + 1 < b1) step(b + 1, k1, v1, k0, v0);
+  for (int sb = sb0 + 1; sb < sb1; sb += 2) {
+    step(sb, false, k1, k0, v1, v0);
+    if (sb + 1 < sb1) step(sb + 1, false, k0, k1, v0, v1);
   }
+  // The last block's P.V: its V went to v0 if the last step was an even
+  // number of steps after the first, else to v1.
+  block_pv<D>(((sb1 - 1 - sb0) & 1 ? v1 : v0) + soff, vl, pb, o, lsum);
+  __syncthreads();
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  // Merge the four streams. Every wave parks its fp32 output tile and its
+  // (reference max, sum) in LDS; then the wave of stream s merges the
+  // 32-dim output tile dt = s of its rows over the streams.
+  const float l_tot = lsum[0];
+  {
+    char* mine = (st == 0 ? k0 : st == 1 ? v0 : st == 2 ? k1 : v1) + rw * C::OB;
+    float4* ob = reinterpret_cast<float4*>(mine);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        ob[(dt * 4 + qd) * 64 + lane] =
+            make_float4(o[dt][4 * qd], o[dt][4 * qd + 1], o[dt][4 * qd + 2], o[dt][4 * qd + 3]);
+    mlx[wave * 64 + lane] = make_float2(m_run, l_tot);
+  }
+  __syncthreads();
+  if (!live || st >= C::DT) return;
+  const int dt = st;
+  float ms[kStreams], ls[kStreams];
+#pragma unroll
+  for (int s = 0; s < kStreams; ++s) {
+    const float2 ml = mlx[(s * kRowWaves + rw) * 64 + lane];
+    ms[s] = ml.x;
+    ls[s] = ml.y;
+  }
+  float M = ms[0];
+#pragma unroll
+  for (int s = 1; s < kStreams; ++s) M = fmaxf(M, ms[s]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float L = 0.f, acc[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kStreams; ++s) {
+    const float w = __builtin_amdgcn_exp2f(ms[s] - Mu);
+    L += w * ls[s];
+    const char* src = (s == 0 ? k0 : s == 1 ? v0 : s == 2 ? k1 : v1) + rw * C::OB;
+    const float4* ob = reinterpret_cast<const float4*>(src);
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const float4 x = ob[(dt * 4 + qd) * 64 + lane];
+      acc[4 * qd] += w * x.x;
+      acc[4 * qd + 1] += w * x.y;
+      acc[4 * qd + 2] += w * x.z;
+      acc[4 * qd + 3] += w * x.w;
+    }
+  }
   if (!row_ok) return;
   if (splits == 1) {
-    const float inv = 1.0f / l_tot;
+    const float inv = 1.0f / L;
     uint16_t* orow = out + ((int64_t)node * Hq + hq) * D;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int d0 = 32 * dt + 8 * qd + 4 * h;
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16_rne(o[dt][4 * qd] * inv) |
-               ((uint32_t)f32_to_bf16_rne(o[dt][4 * qd + 1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16_rne(o[dt][4 * qd + 2] * inv) |
-               ((uint32_t)f32_to_bf16_rne(o[dt][4 * qd + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + d0) = pk;
-      }
+    for (int qd = 0; qd < 4; ++qd) {
+      const int d0 = 32 * dt + 8 * qd + 4 * h;
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16_rne(acc[4 * qd] * inv) |
+             ((uint32_t)f32_to_bf16_rne(acc[4 * qd + 1] * inv) << 16);
+      pk.y = (uint32_t)f32_to_bf16_rne(acc[4 * qd + 2] * inv) |
+             ((uint32_t)f32_to_bf16_rne(acc[4 * qd + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(orow + d0) = pk;
+    }
   } else {
-    const int64_t prow = ((int64_t)split * Hkv + g) * rows_pad + rho;
-    float* po = part_o + prow * D;
+    // Partial tile wb of this split: [DT][4][64 lanes] float4 plus one
+    // (max, sum) pair per row.
+    const int64_t wb = ((int64_t)(split * Hkv + g) * tiles + tile) * kRowWaves + rw;
+    float4* po = reinterpret_cast<float4*>(part_o) + (wb * C::DT + dt) * 4 * 64;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int d0 = 32 * dt + 8 * qd + 4 * h;
-        *reinterpret_cast<float4*>(po + d0) =
-            make_float4(o[dt][4 * qd], o[dt][4 * qd + 1], o[dt][4 * qd + 2], o[dt][4 * qd + 3]);
-      }
-    if (h == 0) *reinterpret_cast<float2*>(part_ml + prow * 2) = make_float2(m_run, l_tot);
+    for (int qd = 0; qd < 4; ++qd)
+      po[qd * 64 + lane] = make_float4(acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]);
+    if (dt == 0 && h == 0) reinterpret_cast<float2*>(part_ml)[wb * 32 + j] = make_float2(M, L);
   }
 }
 
-// Merge the per-split partials of each query row: 32 threads per row, each
-// handling D / 32 consecutive dims. Loads of several splits are issued
-// together (splits are taken in batches of 8) so their latencies overlap.
+// Merge the per-split partials. One thread per float4 of a partial tile
+// (the same slot in every split), so each load instruction of a wave reads
+// 1 KB contiguously; the splits are taken 8 at a time with every load of a
+// batch issued before any is used, merged by a running maximum.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits,
-    int N, int Hq, int Hkv, int rows_pad, uint16_t* __restrict__ out) {
-  constexpr int PD = D / 32;
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int N,
+    int Hq, int Hkv, int tiles, uint16_t* __restrict__ out) {
+  constexpr int DT = D / 32;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int lane = t & 63, qd = (t >> 6) & 3;
+  const int dt = (t >> 8) % DT;
+  const int wbl = t / (256 * DT);  // (kv-head, tile, row wave)
+  const int WB = Hkv * tiles * kRowWaves;
+  if (wbl >= WB) return;
+  const int rw = wbl % kRowWaves, tile = (wbl / kRowWaves) % tiles, g = wbl / (kRowWaves * tiles);
   const int G = Hq / Hkv, R = N * G;
-  const int row = blockIdx.x * 8 + (threadIdx.x >> 5);  // over Hkv * R
-  const int sub = threadIdx.x & 31;
-  if (row >= Hkv * R) return;
-  const int g = row / R, rho = row % R;
-  const int64_t stride = (int64_t)Hkv * rows_pad;  // rows between consecutive splits
-  const int64_t row0 = (int64_t)g * rows_pad + rho;
-  float den = 0.f, acc[PD];
-#pragma unroll
-  for (int i = 0; i < PD; ++i) acc[i] = 0.f;
-  // Splits are taken 8 at a time: every load of a batch is issued before
-  // any of them is used, so their latencies overlap.
-  float M = -INFINITY;
+  const int j = lane & 31, h = lane >> 5;
+  const int rho = tile * kRowsPerTile + rw * 32 + j;
+  if (rho >= R) return;
+  const float4* po = reinterpret_cast<const float4*>(part_o);
+  const float2* pml = reinterpret_cast<const float2*>(part_ml);
+  float M = -INFINITY, L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < splits; s0 += 8) {
     float2 ml[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      ml[u] = s0 + u < splits ? *reinterpret_cast<const float2*>(part_ml + (row0 + (s0 + u) * stride) * 2)
-                              : make_float2(-INFINITY, 0.f);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) M = fmaxf(M, ml[u].x);
-  }
-  for (int s0 = 0; s0 < splits; s0 += 8) {
-    float2 ml[8];
-    float po[8][PD];
+    float4 x[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int sp = s0 + u;
-      const int64_t prow = row0 + (int64_t)(sp < splits ? sp : 0) * stride;
-      ml[u] = *reinterpret_cast<const float2*>(part_ml + prow * 2);
-#pragma unroll
-      for (int i = 0; i < PD; ++i) po[u][i] = part_o[prow * D + PD * sub + i];
+      const int64_t wb = (int64_t)min(s0 + u, splits - 1) * WB + wbl;
+      ml[u] = pml[wb * 32 + j];
+      x[u] = po[((wb * DT + dt) * 4 + qd) * 64 + lane];
     }
+    float bm = M;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < splits) bm = fmaxf(bm, ml[u].x);
+    const float bmu = bm == -INFINITY ? 0.f : bm;
+    const float corr = __builtin_amdgcn_exp2f(M - bmu);  // 0 while M = -inf
+    L *= corr;
+    acc.x *= corr;
+    acc.y *= corr;
+    acc.z *= corr;
+    acc.w *= corr;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (s0 + u < splits) {
-        const float wgt = exp2f(ml[u].x - M);
-        den += wgt * ml[u].y;
-#pragma unroll
-        for (int i = 0; i < PD; ++i) acc[i] += wgt * po[u][i];
+        const float w = __builtin_amdgcn_exp2f(ml[u].x - bmu);
+        L += w * ml[u].y;
+        acc.x += w * x[u].x;
+        acc.y += w * x[u].y;
+        acc.z += w * x[u].z;
+        acc.w += w * x[u].w;
       }
     }
+    M = bm;
   }
-  const float inv = 1.0f / den;
+  const float inv = 1.0f / L;
   const int node = rho / G, hq = g * G + rho % G;
-  uint16_t* orow = out + ((int64_t)node * Hq + hq) * D + PD * sub;
-#pragma unroll
-  for (int i = 0; i < PD; ++i) orow[i] = f32_to_bf16_rne(acc[i] * inv);
+  const int d0 = 32 * dt + 8 * qd + 4 * h;
+  uint2 pk;
+  pk.x = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
+  pk.y = (uint32_t)f32_to_bf16_rne(acc.z * inv) | ((uint32_t)f32_to_bf16_rne(acc.w * inv) << 16);
+  *reinterpret_cast<uint2*>(out + ((int64_t)node * Hq + hq) * D + d0) = pk;
 }
 
-int target_workgroups() {
+// Workgroups the grid aims for: one per CU. DDTREE_ATTN_SLOTS overrides it
+// (for sweeps).
+int attn_slots() {
   static const int t = [] {
-    const char* s = std::getenv("DDTREE_ATTN_TARGET_WG");
+    const char* s = std::getenv("DDTREE_ATTN_SLOTS");
     const int v = s ? std::atoi(s) : 0;
     return v > 0 ? v : 256;
   }();
@@ -455,28 +677,20 @@ int target_workgroups() {
 namespace ddt_host {
 
 AttnPlan attn_plan(int N, int Hq, int Hkv, int D, int S) {
-  (void)D;
   AttnPlan p;
   const int G = Hq / Hkv, R = N * G;
   p.tiles = (R + kRowsPerTile - 1) / kRowsPerTile;
   p.rows_pad = p.tiles * kRowsPerTile;
-  const int NB = (S + N + kBK - 1) / kBK;
-  const int target = target_workgroups();
-  // Pick blocks per split so that the grid is close to the target size,
-  // preferring split counts that allow the XCD-aware mapping.
-  int best_bps = NB, best_score = 1 << 30;
-  for (int bps = 1; bps <= NB; ++bps) {
-    const int splits = (NB + bps - 1) / bps;
-    const int wgs = Hkv * p.tiles * splits;
-    const bool xcd = (Hkv * splits) % kXcds == 0;
-    const int score = (wgs > target ? wgs - target : target - wgs) + (xcd ? 0 : target / 4);
-    if (score < best_score) {
-      best_score = score;
-      best_bps = bps;
-    }
-  }
-  p.blocks_per_split = best_bps;
-  p.splits = (NB + best_bps - 1) / best_bps;
+  const int NSB = (S + N + kSBK - 1) / kSBK;
+  const int per_split = Hkv * p.tiles;
+  // As many splits as keep the grid within one workgroup per CU; then even
+  // out the superblocks per split.
+  int splits = attn_slots() / per_split;
+  splits = splits < 1 ? 1 : (splits > NSB ? NSB : splits);
+  p.sb_per_split = (NSB + splits - 1) / splits;
+  p.splits = (NSB + p.sb_per_split - 1) / p.sb_per_split;
+  p.wgs = per_split * p.splits;
+  p.per_xcd = (p.wgs + kXcds - 1) / kXcds;
   if (p.splits == 1) {
     p.part_o_off = p.part_ml_off = p.bytes = 0;
   } else {
@@ -495,28 +709,26 @@ int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int S, 
   float* po = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_o_off) : nullptr;
   float* pml = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_ml_off) : nullptr;
   const float scale_log2 = scale * 1.4426950408889634f;
-  const int groups = Hkv * p.splits;
-  const int xcd_map = groups % kXcds == 0 ? 1 : 0;
-  const dim3 grid(groups * p.tiles);
+  const dim3 grid(kXcds * p.per_xcd);
   if (D == 128) {
     hipLaunchKernelGGL(tree_attn_kernel<128>, grid, dim3(kThreads), 0, stream, q, k, v, S, S_cap,
                        N, Hq, Hkv, scale_log2, anc, W, out, po, pml, p.tiles, p.splits,
-                       p.blocks_per_split, p.rows_pad, xcd_map);
+                       p.sb_per_split, p.wgs, p.per_xcd);
   } else {
     hipLaunchKernelGGL(tree_attn_kernel<64>, grid, dim3(kThreads), 0, stream, q, k, v, S, S_cap,
                        N, Hq, Hkv, scale_log2, anc, W, out, po, pml, p.tiles, p.splits,
-                       p.blocks_per_split, p.rows_pad, xcd_map);
+                       p.sb_per_split, p.wgs, p.per_xcd);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return launch_status(e);
-  const int rows = Hkv * N * (Hq / Hkv);
-  const dim3 cgrid((rows + 7) / 8);
+  const int threads = Hkv * p.tiles * kRowWaves * (D / 32) * 4 * 64;
+  const dim3 cgrid((threads + 255) / 256);
   if (D == 128) {
     hipLaunchKernelGGL(tree_attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, po, pml,
-                       p.splits, N, Hq, Hkv, p.rows_pad, out);
+                       p.splits, N, Hq, Hkv, p.tiles, out);
   } else {
     hipLaunchKernelGGL(tree_attn_combine_kernel<64>, cgrid, dim3(256), 0, stream, po, pml,
-                       p.splits, N, Hq, Hkv, p.rows_pad, out);
+                       p.splits, N, Hq, Hkv, p.tiles, out);
   }
   return launch_status(hipGetLastError());
 }

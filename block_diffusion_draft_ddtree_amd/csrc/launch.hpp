@@ -24,7 +24,9 @@ int build_launch(const float* logp, const int32_t* token, int L, int K, int B,
 
 // ddtree_tree_attn: grid shape and split-partial workspace.
 struct AttnPlan {
-  int tiles, splits, blocks_per_split, rows_pad;
+  int tiles, rows_pad;       // 64-row query tiles per kv-head
+  int splits, sb_per_split;  // key range cut into splits of 128-key superblocks
+  int wgs, per_xcd;          // workgroups with work; grid = 8 * per_xcd
   size_t part_o_off, part_ml_off, bytes;
 };
 AttnPlan attn_plan(int N, int Hq, int Hkv, int D, int S);
