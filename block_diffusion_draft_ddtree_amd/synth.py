@@ -150,8 +150,13 @@ def drafter_logits(w: Workload, round_idx: int = 0) -> Logits:
     """Per-position drafter logits of the workload's family.
 
     tiny:   2*N(0,1) plus +6 on one uniform peak token per position.
-    peaked: 2*N(0,1) plus (9 - 0.4 i) on a peak and (7 - 0.4 i) on a
-            distinct runner-up token at 0-based block position i.
+    peaked: a confident drafter: N(0,1) bulk, and at 0-based block position
+            i a peak token with probability p_peak(i) = max(0.85 - 0.03 i,
+            0.2) and a distinct runner-up with p_run(i) = 0.08 + 0.005 i
+            (their logits are set from the bulk's own partition sum, so the
+            softmax gives these probabilities); confidence decays along the
+            block, and best-first trees grow deep along the peak path with
+            branches near the root.
     flat:   1.5*N(0,1) plus +3 on one peak token.
     """
     g = rng(w.family, round_idx, STREAM_LOGITS)
@@ -162,13 +167,17 @@ def drafter_logits(w: Workload, round_idx: int = 0) -> Logits:
         x[np.arange(L), peak] += np.float32(6.0)
         return Logits(x, peak, None)
     if w.logits == "peaked":
-        x = np.float32(2.0) * g.standard_normal((L, V), dtype=np.float32)
+        x = g.standard_normal((L, V), dtype=np.float32)
         peak = g.integers(0, V, size=L)
         off = g.integers(1, V, size=L)
         runner = (peak + off) % V
-        i = np.arange(L, dtype=np.float32)
-        x[np.arange(L), peak] += (np.float32(9.0) - np.float32(0.4) * i).astype(np.float32)
-        x[np.arange(L), runner] += (np.float32(7.0) - np.float32(0.4) * i).astype(np.float32)
+        rows = np.arange(L)
+        p_peak, p_run = peaked_probs(L)
+        e = np.exp(x.astype(np.float64))
+        z = e.sum(axis=1) - e[rows, peak] - e[rows, runner]  # bulk partition sum
+        rest = 1.0 - p_peak - p_run
+        x[rows, peak] = np.log(p_peak * z / rest).astype(np.float32)
+        x[rows, runner] = np.log(p_run * z / rest).astype(np.float32)
         return Logits(x, peak, runner)
     if w.logits == "flat":
         x = np.float32(1.5) * g.standard_normal((L, V), dtype=np.float32)
@@ -176,6 +185,13 @@ def drafter_logits(w: Workload, round_idx: int = 0) -> Logits:
         x[np.arange(L), peak] += np.float32(3.0)
         return Logits(x, peak, None)
     raise ValueError(w.logits)
+
+
+def peaked_probs(L: int):
+    """Target probabilities of the peak and runner-up tokens per block
+    position of the 'peaked' drafter."""
+    i = np.arange(L, dtype=np.float64)
+    return np.maximum(0.85 - 0.03 * i, 0.2), 0.08 + 0.005 * i
 
 
 def tie_logits(L: int, V: int, g: np.random.Generator, levels: int = 4) -> np.ndarray:
