@@ -8,10 +8,18 @@ the Qwen3-Coder-30B-A3B verifier shape (32 q-heads / 4 kv-heads, head dim
 B = 64. Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--graph]
+    python bench.py --copy-probe     # plain device copy of known size (for
+                                     # scaling the HBM byte counters)
+
+roofline.traffic is the measured HBM bytes of one ddtree_tree_attn call
+(both of its kernels), read from the counter summary under profiles/ when
+that summary was taken on the current attention source (its sha256 is
+recorded there); otherwise null.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -21,6 +29,48 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+ATTN_SOURCE = os.path.join(ROOT, "block_diffusion_draft_ddtree_amd", "csrc", "attn.hip")
+COPY_PROBE_BYTES = 256 << 20  # bytes read and bytes written by the copy probe
+
+
+def traffic_summary_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"tree_attn_{workload}_traffic.txt")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per ddtree_tree_attn call from the committed counter
+    summary, or None when there is none or it predates the current kernel
+    source."""
+    path = traffic_summary_path(workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    with open(ATTN_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("attn_source_sha256") != sha or "traffic_bytes_per_call" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_call"])
+
+
+def copy_probe():
+    """A plain device-to-device copy of COPY_PROBE_BYTES, five times: what
+    FETCH_SIZE and WRITE_SIZE read for it gives their scale to bytes."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = COPY_PROBE_BYTES // 4
+    src = torch.arange(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    assert bool(torch.equal(dst[-8:], src[-8:]))
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "launches": 5}), flush=True)
 
 
 def parse():
@@ -32,6 +82,8 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay the round as a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=30)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only the plain copy used to scale the byte counters")
     return ap.parse_args()
 
 
@@ -60,6 +112,9 @@ def main():
         print("bench.py measures one GPU only: the hot path runs on a single MI355X "
               "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
 
     import torch
 
@@ -182,7 +237,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name)
     roof["kernel"] = "ddtree_tree_attn"
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops

@@ -88,6 +88,9 @@ QWEN3_8B = _w("qwen3_8b", "qwen3_8b", L=16, V=151936, K=64, B=64, Hq=32,
 CODER30B_B64 = _w("coder30b_b64", "coder30b", L=16, V=151936, K=64, B=64,
                   Hq=32, Hkv=4, D=128, S=4096, layers=48, logits="peaked")
 CODER30B_B256 = replace(CODER30B_B64, name="coder30b_b256", K=256, B=256)
+# The same verifier shape with a confident drafter (deep trees, accepted
+# length ~4): exercises deep ancestor masks, the walk and the compaction.
+CODER30B_B64_DEEP = replace(CODER30B_B64, name="coder30b_b64_deep", logits="confident")
 LONGCTX = _w("longctx", "longctx", L=16, V=151936, K=256, B=256, Hq=32,
              Hkv=4, D=128, S=32768, layers=1, logits="peaked")
 SWEEP_BUDGETS = (16, 32, 64, 128, 256, 512)
@@ -99,7 +102,7 @@ def sweep(B: int) -> Workload:
 
 
 WORKLOADS = {w.name: w for w in
-             (TINY, QWEN3_8B, CODER30B_B64, CODER30B_B256, LONGCTX)}
+             (TINY, QWEN3_8B, CODER30B_B64, CODER30B_B256, CODER30B_B64_DEEP, LONGCTX)}
 for _b in SWEEP_BUDGETS:
     WORKLOADS[f"sweep_b{_b}"] = sweep(_b)
 
@@ -150,13 +153,17 @@ def drafter_logits(w: Workload, round_idx: int = 0) -> Logits:
     """Per-position drafter logits of the workload's family.
 
     tiny:   2*N(0,1) plus +6 on one uniform peak token per position.
-    peaked: a confident drafter: N(0,1) bulk, and at 0-based block position
-            i a peak token with probability p_peak(i) = max(0.85 - 0.03 i,
-            0.2) and a distinct runner-up with p_run(i) = 0.08 + 0.005 i
-            (their logits are set from the bulk's own partition sum, so the
-            softmax gives these probabilities); confidence decays along the
-            block, and best-first trees grow deep along the peak path with
-            branches near the root.
+    peaked: 2*N(0,1) plus (9 - 0.4 i) on a peak and (7 - 0.4 i) on a
+            distinct runner-up token at 0-based block position i. Over
+            V = 151936 the bulk carries most of the mass (the peak gets
+            q ~ 0.01), so best-first trees of B = 64 stay at depth 1.
+    confident: a confident drafter: N(0,1) bulk, and at position i a peak
+            token with probability p_peak(i) = max(0.85 - 0.03 i, 0.2) and a
+            distinct runner-up with p_run(i) = 0.08 + 0.005 i (their logits
+            are set from the bulk's own partition sum, so the softmax gives
+            these probabilities). Confidence decays along the block, and
+            best-first trees grow deep along the peak path with branches
+            near the root.
     flat:   1.5*N(0,1) plus +3 on one peak token.
     """
     g = rng(w.family, round_idx, STREAM_LOGITS)
@@ -167,12 +174,21 @@ def drafter_logits(w: Workload, round_idx: int = 0) -> Logits:
         x[np.arange(L), peak] += np.float32(6.0)
         return Logits(x, peak, None)
     if w.logits == "peaked":
+        x = np.float32(2.0) * g.standard_normal((L, V), dtype=np.float32)
+        peak = g.integers(0, V, size=L)
+        off = g.integers(1, V, size=L)
+        runner = (peak + off) % V
+        i = np.arange(L, dtype=np.float32)
+        x[np.arange(L), peak] += (np.float32(9.0) - np.float32(0.4) * i).astype(np.float32)
+        x[np.arange(L), runner] += (np.float32(7.0) - np.float32(0.4) * i).astype(np.float32)
+        return Logits(x, peak, runner)
+    if w.logits == "confident":
         x = g.standard_normal((L, V), dtype=np.float32)
         peak = g.integers(0, V, size=L)
         off = g.integers(1, V, size=L)
         runner = (peak + off) % V
         rows = np.arange(L)
-        p_peak, p_run = peaked_probs(L)
+        p_peak, p_run = confident_probs(L)
         e = np.exp(x.astype(np.float64))
         z = e.sum(axis=1) - e[rows, peak] - e[rows, runner]  # bulk partition sum
         rest = 1.0 - p_peak - p_run
@@ -187,9 +203,9 @@ def drafter_logits(w: Workload, round_idx: int = 0) -> Logits:
     raise ValueError(w.logits)
 
 
-def peaked_probs(L: int):
+def confident_probs(L: int):
     """Target probabilities of the peak and runner-up tokens per block
-    position of the 'peaked' drafter."""
+    position of the 'confident' drafter."""
     i = np.arange(L, dtype=np.float64)
     return np.maximum(0.85 - 0.03 * i, 0.2), 0.08 + 0.005 * i
 

@@ -31,13 +31,26 @@ def test_peaked_generator_shape():
     lg = synth.drafter_logits(w)
     assert lg.x.shape == (16, 151936) and lg.x.dtype == np.float32
     assert np.all(lg.peak != lg.runner)
+    # Regenerating the unboosted bulk from the same stream isolates the boosts.
+    g = synth.rng(w.family, 0, synth.STREAM_LOGITS)
+    bulk = np.float32(2.0) * g.standard_normal((16, 151936), dtype=np.float32)
+    i = np.arange(16)
+    np.testing.assert_allclose(lg.x[i, lg.peak] - bulk[i, lg.peak], 9.0 - 0.4 * i, atol=1e-5)
+    np.testing.assert_allclose(lg.x[i, lg.runner] - bulk[i, lg.runner], 7.0 - 0.4 * i, atol=1e-5)
+
+
+def test_confident_generator():
+    w = synth.CODER30B_B64_DEEP
+    lg = synth.drafter_logits(w)
+    assert lg.x.shape == (16, 151936) and lg.x.dtype == np.float32
+    assert np.all(lg.peak != lg.runner)
     # The softmax (fp64) of each row gives the designed peak and runner-up
     # probabilities, and every other token keeps its N(0,1) bulk logit.
     x = lg.x.astype(np.float64)
     q = np.exp(x - x.max(axis=1, keepdims=True))
     q /= q.sum(axis=1, keepdims=True)
     i = np.arange(16)
-    p_peak, p_run = synth.peaked_probs(16)
+    p_peak, p_run = synth.confident_probs(16)
     np.testing.assert_allclose(q[i, lg.peak], p_peak, rtol=1e-5)
     np.testing.assert_allclose(q[i, lg.runner], p_run, rtol=1e-5)
     assert np.all(p_peak[:-1] > p_peak[1:])  # confidence decays along the block
