@@ -60,6 +60,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
@@ -71,6 +72,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerTile = 32 * kRowWaves;
 constexpr int kSBK = kBK * kStreams;          // keys per superblock
 constexpr int kXcds = 8;
+constexpr int kMaxMaskWords = (DDTREE_MAX_B + 1 + 31) / 32;  // words of an ancestor row
 
 template <int D>
 struct Cfg {
@@ -283,21 +285,16 @@ __device__ __forceinline__ void block_pv(const char* Vb, const VLanes<D>& vl, co
   }
 }
 
-// S^T = K Q^T for this wave's 32 query columns over one 32-key block, and,
-// when `pv`, the P.V products of the previous block at the same time: the
-// dependent chain of Q.K products and the independent P.V products
-// alternate on the matrix core, and the softmax of this block (vector ALU)
-// can then run while the last of them finish.
+// S^T = K Q^T for this wave's 32 query columns over one 32-key block: one
+// chain of products, with the K operand reads kept a few steps ahead.
 template <int D>
-__device__ __forceinline__ f32x16 block_qk_pv(const char* Kb, const char* Vb, bool pv,
-                                              const bf16x8 (&qf)[Cfg<D>::KS], const PBlock& pb,
-                                              const VLanes<D>& vl, f32x16 (&o)[Cfg<D>::DT],
-                                              f32x16& lsum, int lane) {
+__device__ __forceinline__ f32x16 block_qk(const char* Kb, const bf16x8 (&qf)[Cfg<D>::KS],
+                                           int lane) {
   using C = Cfg<D>;
-  static_assert(C::KS == 2 * C::DT, "one P.V product per Q.K step");
   const int j = lane & 31, h = lane >> 5;
   const char* krow = Kb + j * C::ROWB;
   const int f = fk<D>(j);
+  constexpr int AHEAD = C::KS / 2;
   bf16x8 ka[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks)
@@ -305,49 +302,40 @@ __device__ __forceinline__ f32x16 block_qk_pv(const char* Kb, const char* Vb, bo
   f32x16 sacc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-  if (pv) {
-    bf16x8 va[2][C::DT];
-    read_v<D>(Vb, vl, va);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sacc, 0, 0, 0);
-      const int mm = ks / C::DT, dt = ks % C::DT;
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mm][dt], pb.p[mm], o[dt], 0, 0, 0);
-    }
-    const bf16x8 ones = bf16_ones();
-    lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb.p[0], lsum, 0, 0, 0);
-    lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb.p[1], lsum, 0, 0, 0);
-    // Schedule: the reads of two steps ahead (one K read and two V reads per
-    // step), then per step its two products and the next step's reads; this
-    // keeps few operands live at once.
-    constexpr int AH = 2;
-    __builtin_amdgcn_sched_group_barrier(0x100, 3 * AH, 0);
+  for (int ks = 0; ks < C::KS; ++ks)
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sacc, 0, 0, 0);
+  // Schedule: AHEAD reads, then alternate one product with one read.
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
-    for (int i = 0; i < C::KS - AH; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * AH + 2, 0);
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sacc, 0, 0, 0);
+  for (int i = 0; i < C::KS - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
   return sacc;
 }
 
 // Online softmax of one block's scores (unscaled until the exponent, where
-// scale * log2(e) and the reference maximum enter as one fma). For blocks
-// reaching past S, `vis` (block_visibility) masks the scores by a
-// wave-uniform branch that touches only the scores. Rescaling multiplies
-// the running output and sums, so it must come after the previous block's
-// P.V products are issued (the hardware orders the two).
-template <int D>
-__device__ __forceinline__ PBlock block_softmax(f32x16 sacc, f32x16 (&o)[Cfg<D>::DT],
-                                                float& m_run, f32x16& lsum, float c, int lane,
-                                                bool masked, uint32_t vis) {
+// scale * log2(e) and the reference maximum enter as one fma), fused with
+// the P.V products of the previous block when PV: those products do not
+// depend on this block's exponentials, so the matrix core works through
+// them while the vector ALU computes the exponentials. A rescale (rare:
+// lazy, see kRescaleSlack) multiplies the running output and sums before
+// the previous block's products are added, so it also scales that block's
+// pending weights (they were formed against the old reference maximum).
+// For blocks reaching past S, `vis` (block_visibility) masks the scores by
+// a wave-uniform branch that touches only the scores.
+template <int D, bool PV>
+__device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
+                                                 const VLanes<D>& vl, PBlock& pb,
+                                                 f32x16 (&o)[Cfg<D>::DT], float& m_run,
+                                                 f32x16& lsum, float c, int lane, bool masked,
+                                                 uint32_t vis) {
   using C = Cfg<D>;
   const int h = lane >> 5;
+  bf16x8 va[2][C::DT];
+  if (PV) read_v<D>(Vprev, vl, va);
   if (masked) {
     const uint32_t vh = vis >> (4 * h);
 #pragma unroll
@@ -369,16 +357,37 @@ __device__ __forceinline__ PBlock block_softmax(f32x16 sacc, f32x16 (&o)[Cfg<D>:
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][r] *= corr;
+    if (PV) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        pb.p[e >> 3][e & 7] = (__bf16)((float)pb.p[e >> 3][e & 7] * corr);
+    }
     m_run = m_new;
+  }
+  if (PV) {
+    const bf16x8 ones = bf16_ones();
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mm][dt], pb.p[mm], o[dt], 0, 0, 0);
+      lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb.p[mm], lsum, 0, 0, 0);
+    }
   }
   // A column that has seen no visible key yet keeps m_run = -inf; use 0 as
   // its reference so that masked weights come out as exp2(-inf) = 0.
   const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-  PBlock pb;
 #pragma unroll
   for (int r = 0; r < 16; ++r)
     pb.p[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[r], c, neg_m));
-  return pb;
+  if (PV) {
+    // Interleave: one product, then a slice of the vector work.
+#pragma unroll
+    for (int i = 0; i < 2 * C::DT + 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
+    }
+  }
 }
 
 template <int D>
@@ -398,6 +407,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(1024))) char k1[C::STAGEB];
   __shared__ __attribute__((aligned(1024))) char v1[C::STAGEB];
   __shared__ float2 mlx[kWaves * 64];
+  __shared__ uint32_t mrows[kRowsPerTile * kMaxMaskWords];
 
   // Workgroup id -> position in the (kv-head, split, tile) order, one
   // contiguous run per XCD. Ids past the work exit before any barrier.
@@ -427,21 +437,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int sb1 = min(NSB, sb0 + sb_per_split);
   const uint16_t* kh = k + (int64_t)g * S_cap * D;
   const uint16_t* vh = v + (int64_t)g * S_cap * D;
-  const uint32_t* arow = anc + (int64_t)node * W;
   const int soff = st * C::TILEB;
 
-  // The two mask words of a block are loaded one superblock ahead, before
-  // that superblock's copy, so they have always arrived when the block is
-  // computed and no wait for them can stall on an in-flight copy.
-  uint32_t mw0_n = 0u, mw1_n = 0u;
-  auto fetch_mask = [&](int key0) {
-    mw0_n = mw1_n = 0u;
-    if (key0 + kBK > S && key0 < KT && row_ok) {
-      const int wlo = max(0, key0 - S) >> 5;
-      mw0_n = wlo < W ? arow[wlo] : 0u;
-      mw1_n = wlo + 1 < W ? arow[wlo + 1] : 0u;
-    }
-  };
   const CopyLanes<D> cl = copy_lanes<D>(rw, lane);
   // Blocks wholly past the last key are still copied (every row clamped to
   // the last key) and computed (every key masked): every wave then runs one
@@ -454,22 +451,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     copy_block<D, true>(vh, (sb * kStreams + st) * kBK, KT, dst + soff, rw, cl);
   };
   const VLanes<D> vl = v_lanes<D>(lane);
-  fetch_mask((sb0 * kStreams + st) * kBK);
   copy_k(sb0, k0);
-
-  bf16x8 qf[C::KS];
+  // Q of the tile goes through LDS too: the 32 rows of row wave rw land in
+  // k1 (free until step 0 copies into it) laid out like a K block, copied
+  // by that row wave's four stream waves with whole-row coalesced reads
+  // (lanes holding Q^T operands would each touch a different row). Rows
+  // past R are clamped to row R - 1: finite data whose results are dropped.
   {
-    const uint16_t* qrow = q + ((int64_t)node * Hq + hq) * D + 8 * h;
+    constexpr int QC = C::TILEB / 1024 / kStreams;  // copies per wave
+    char* qdst = k1 + rw * C::TILEB;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      if (row_ok) {
-        qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.0f;
-      }
+    for (int i = 0; i < QC; ++i) {
+      const int copy = st * QC + i;
+      const int row = copy * C::ROWS_PER_COPY + lane / C::NS;
+      const int rr = min(row0 + row, R - 1);
+      const int qrow = (rr / G) * Hq + g * G + rr % G;
+      const char* src = reinterpret_cast<const char*>(q + (int64_t)qrow * D) +
+                        16 * ((lane % C::NS) ^ fk<D>(row));
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(qdst + copy * 1024), 16, 0, 0);
     }
   }
+  // Ancestor rows of the tile's 64 query rows (row r: node (tile_row0 + r)
+  // / G, clamped to the last row), staged in LDS when the workgroup's key
+  // range reaches the tree block, after the copies above are on their way;
+  // a masked block then reads its two words from LDS. Only the Wn =
+  // ceil(N / 32) words that can hold a node are kept.
+  const int Wn = (N + 31) >> 5;
+  const int tile_row0 = tile * kRowsPerTile;
+  if (sb1 * kSBK > S) {
+    for (int i = threadIdx.x; i < kRowsPerTile * Wn; i += kThreads) {
+      const int r = i / Wn, w = i - r * Wn;
+      const int rr = min(tile_row0 + r, R - 1);
+      mrows[i] = anc[(int64_t)(rr / G) * W + w];
+    }
+  }
+  const uint32_t* myrow = mrows + (rw * 32 + j) * Wn;
+  auto vis_of = [&](int key0) {
+    if (key0 + kBK <= S) return ~0u;
+    const int wlo = max(0, key0 - S) >> 5;
+    const uint32_t mw0 = wlo < Wn ? myrow[wlo] : 0u;
+    const uint32_t mw1 = wlo + 1 < Wn ? myrow[wlo + 1] : 0u;
+    return block_visibility(key0, S, N, mw0, mw1);
+  };
 
   f32x16 o[C::DT];
 #pragma unroll
@@ -483,6 +506,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // Q^T operands of the wave's 32 rows, read like a K operand; then a
+  // barrier before step 0 copies into k1.
+  bf16x8 qf[C::KS];
+  {
+    const char* qrow = k1 + rw * C::TILEB + j * C::ROWB;
+    const int f = fk<D>(j);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ((2 * ks + h) ^ f));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   // Software pipeline over superblocks. Step i forms the scores of block i
   // and its softmax weights, and issues the P.V products of block i - 1
@@ -493,21 +528,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // are peeled; the loop is unrolled by two so every access names a fixed
   // array.
   PBlock pb;  // weights of the previous block
-  auto vis_of = [&](int key0, uint32_t mw0, uint32_t mw1) {
-    return key0 + kBK > S ? block_visibility(key0, S, N, mw0, mw1) : ~0u;
-  };
   auto step = [&](int sb, bool first, const char* kc, char* kn, char* vdst, const char* vprev) {
-    const uint32_t mw0 = mw0_n, mw1 = mw1_n;
-    if (sb + 1 < sb1) {
-      fetch_mask(((sb + 1) * kStreams + st) * kBK);
-      copy_k(sb + 1, kn);
-    }
+    if (sb + 1 < sb1) copy_k(sb + 1, kn);
     copy_v(sb, vdst);
     const int key0 = (sb * kStreams + st) * kBK;
-    const f32x16 sacc =
-        block_qk_pv<D>(kc + soff, vprev + soff, !first, qf, pb, vl, o, lsum, lane);
-    pb = block_softmax<D>(sacc, o, m_run, lsum, scale_log2, lane, key0 + kBK > S,
-                          vis_of(key0, mw0, mw1));
+    const f32x16 sacc = block_qk<D>(kc + soff, qf, lane);
+    const bool masked = key0 + kBK > S;
+    const uint32_t vis = vis_of(key0);
+    if (first)
+      block_softmax_pv<D, false>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
+                                 masked, vis);
+    else
+      block_softmax_pv<D, true>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
+                                masked, vis);
+    // Keep the wait for the copies at the end of the step: the scheduler
+    // would otherwise hoist it (and the barrier) above the vector work.
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -585,12 +621,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   } else {
     // Partial tile wb of this split: [DT][4][64 lanes] float4 plus one
-    // (max, sum) pair per row.
+    // (max, sum) pair per row. Non-temporal stores: the partials are read
+    // once, by the combine kernel, and need not sit in L2 (whose dirty lines
+    // would otherwise be written back at the end of the kernel).
     const int64_t wb = ((int64_t)(split * Hkv + g) * tiles + tile) * kRowWaves + rw;
-    float4* po = reinterpret_cast<float4*>(part_o) + (wb * C::DT + dt) * 4 * 64;
+    f32x4* po = reinterpret_cast<f32x4*>(part_o) + (wb * C::DT + dt) * 4 * 64;
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd)
-      po[qd * 64 + lane] = make_float4(acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]);
+      __builtin_nontemporal_store(
+          f32x4{acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]},
+          po + qd * 64 + lane);
     if (dt == 0 && h == 0) reinterpret_cast<float2*>(part_ml)[wb * 32 + j] = make_float2(M, L);
   }
 }
