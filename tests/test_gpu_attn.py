@@ -108,7 +108,8 @@ def test_planted_keys_order_one_outputs():
     _run(q_bits, q, kv_bits, kv, S, anc, scale=2.0)
 
 
-@pytest.mark.parametrize("name", ["coder30b_b64", "qwen3_8b", "coder30b_b256"])
+@pytest.mark.parametrize("name", ["coder30b_b64", "qwen3_8b", "coder30b_b256", "coder30b_b64_deep",
+                                  "sweep_b512"])
 def test_full_workload_sampled(name):
     w = synth.WORKLOADS[name]
     lg = synth.drafter_logits(w)

@@ -62,8 +62,9 @@ def test_walk_random_targets_and_full_depth():
     assert _walk(chain, tgt, L) == L
 
 
-def test_walk_coder30b_follow_peak():
-    w = synth.CODER30B_B64
+@pytest.mark.parametrize("name", ["coder30b_b64", "coder30b_b64_deep"])
+def test_walk_coder30b_follow_peak(name):
+    w = synth.WORKLOADS[name]
     lg = synth.drafter_logits(w)
     lp, tok = st.topk(lg.x, w.K)
     tree = ot.build_tree(lp.astype(np.float32), tok, w.B, 0)
