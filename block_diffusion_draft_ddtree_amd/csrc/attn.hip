@@ -326,12 +326,12 @@ __device__ __forceinline__ f32x16 block_qk(const char* Kb, const bf16x8 (&qf)[Cf
 // pending weights (they were formed against the old reference maximum).
 // For blocks reaching past S, `vis` (block_visibility) masks the scores by
 // a wave-uniform branch that touches only the scores.
-template <int D, bool PV>
+template <int D, bool PV, class Mid>
 __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
                                                  const VLanes<D>& vl, PBlock& pb,
                                                  f32x16 (&o)[Cfg<D>::DT], float& m_run,
                                                  f32x16& lsum, float c, int lane, bool masked,
-                                                 uint32_t vis) {
+                                                 uint32_t vis, Mid mid) {
   using C = Cfg<D>;
   const int h = lane >> 5;
   bf16x8 va[2][C::DT];
@@ -364,6 +364,11 @@ __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
     }
     m_run = m_new;
   }
+  // Work handed in by the caller (copies) goes here, between the score
+  // reduction and the products.
+  __builtin_amdgcn_sched_barrier(0);
+  mid();
+  __builtin_amdgcn_sched_barrier(0);
   if (PV) {
     const bf16x8 ones = bf16_ones();
 #pragma unroll
@@ -529,18 +534,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // array.
   PBlock pb;  // weights of the previous block
   auto step = [&](int sb, bool first, const char* kc, char* kn, char* vdst, const char* vprev) {
-    if (sb + 1 < sb1) copy_k(sb + 1, kn);
-    copy_v(sb, vdst);
     const int key0 = (sb * kStreams + st) * kBK;
     const f32x16 sacc = block_qk<D>(kc + soff, qf, lane);
+    // The copies enter the texture-address unit at 64 B per clock, and a
+    // wave whose copies are queued there cannot issue further; so they are
+    // spread over the step: K once the Q.K products are under way, V
+    // between the score reduction and the products.
+    __builtin_amdgcn_sched_barrier(0);
+    if (sb + 1 < sb1) copy_k(sb + 1, kn);
+    __builtin_amdgcn_sched_barrier(0);
+    auto mid = [&]() { copy_v(sb, vdst); };
     const bool masked = key0 + kBK > S;
     const uint32_t vis = vis_of(key0);
     if (first)
       block_softmax_pv<D, false>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
-                                 masked, vis);
+                                 masked, vis, mid);
     else
       block_softmax_pv<D, true>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
-                                masked, vis);
+                                masked, vis, mid);
     // Keep the wait for the copies at the end of the step: the scheduler
     // would otherwise hoist it (and the barrier) above the vector work.
     __builtin_amdgcn_sched_barrier(0);
