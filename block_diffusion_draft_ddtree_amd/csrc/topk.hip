@@ -31,7 +31,7 @@ constexpr int kPerThread = 16;
 constexpr int kChunk = kChunkThreads * kPerThread;  // 4096
 constexpr int kLooseExtra = 256;                     // slots beyond K per chunk
 constexpr int kMergeThreads = 1024;
-constexpr int kSurvCap = 8192;                       // survivors ranked in LDS
+constexpr int kSurvCap = 16384;                      // survivors selected in LDS (128 KB)
 constexpr int kLoadBatch = 8;                        // candidates loaded per thread at once
 
 // Larger digit = closer to the reference maximum (monotone in x).
@@ -45,6 +45,32 @@ __device__ __forceinline__ uint32_t rel_digit(float ref_max, float x) {
 // a before b in rank order: larger logit first, then smaller id.
 __device__ __forceinline__ bool beats(float xa, int ia, float xb, int ib) {
   return xa > xb || (xa == xb && ia < ib);
+}
+
+// Rank of (xt, it) among xs/is[0, n) (how many beat it), n a multiple of 16
+// (pad with sentinels that beat nothing: -inf logit, largest id). Sixteen
+// candidates per iteration with 16-byte LDS reads, so the reads of an
+// iteration are in flight together.
+__device__ __forceinline__ int rank_among(const float* xs, const int* is, int n, float xt,
+                                          int it) {
+  int rank = 0;
+  for (int u = 0; u < n; u += 16) {
+    float4 xa[4];
+    int4 ia[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      xa[q] = *reinterpret_cast<const float4*>(xs + u + 4 * q);
+      ia[q] = *reinterpret_cast<const int4*>(is + u + 4 * q);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      rank += beats(xa[q].x, ia[q].x, xt, it);
+      rank += beats(xa[q].y, ia[q].y, xt, it);
+      rank += beats(xa[q].z, ia[q].z, xt, it);
+      rank += beats(xa[q].w, ia[q].w, xt, it);
+    }
+  }
+  return rank;
 }
 
 struct SelShared {
@@ -263,10 +289,10 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
 struct MergeLds {
   SelShared sh;
   int offs[kMergeThreads + 1];  // exclusive prefix of chunk counts (C <= 1024)
-  float sx[kSurvCap];
-  int si[kSurvCap];
-  float wx[DDTREE_MAX_K];
-  int wi[DDTREE_MAX_K];
+  alignas(16) float sx[kSurvCap];
+  alignas(16) int si[kSurvCap];
+  alignas(16) float wx[DDTREE_MAX_K];
+  alignas(16) int wi[DDTREE_MAX_K];
   float lse, tau, M;
   int total;
   uint32_t nsurv, nwin;
@@ -285,9 +311,15 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
 
   // Chunk metadata: prefix offsets of the candidate lists, lse and tau.
   if (t < 64) {
+    // One chunk per lane per round; the first round's stats and counts
+    // (C <= 64 in the common case) are loaded once and kept.
+    const float4 v0 = lane < C ? st[lane] : make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
+    const int n0 = lane < C ? cnt[lane] : 0;
     float M = -INFINITY, tau = -INFINITY;
     for (int c0 = 0; c0 < C; c0 += 64) {
-      const float4 v = c0 + lane < C ? st[c0 + lane] : make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
+      const float4 v = c0 == 0 ? v0
+                               : (c0 + lane < C ? st[c0 + lane]
+                                                : make_float4(-INFINITY, 0.f, -INFINITY, 0.f));
       M = fmaxf(M, ddt::wave_reduce_uniform(v.x, ddt::OpMax()));
       tau = fmaxf(tau, ddt::wave_reduce_uniform(v.z, ddt::OpMax()));
     }
@@ -295,9 +327,9 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     int carry = 0;
     for (int c0 = 0; c0 < C; c0 += 64) {
       const int c = c0 + lane;
-      const float4 v = c < C ? st[c] : make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
+      const float4 v = c0 == 0 ? v0 : (c < C ? st[c] : make_float4(-INFINITY, 0.f, -INFINITY, 0.f));
       S += ddt::wave_reduce_uniform(c < C ? v.y * expf(v.x - M) : 0.f, ddt::OpSum());
-      int x = c < C ? cnt[c] : 0;
+      int x = c0 == 0 ? n0 : (c < C ? cnt[c] : 0);
       int incl = x;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -366,11 +398,16 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
 
   if (nsurv <= kMergeThreads) {
     // Rank every survivor among the survivors; ranks below K are outputs.
+    const int npad = (nsurv + 15) & ~15;
+    if (t >= nsurv && t < npad) {
+      s.sx[t] = -INFINITY;
+      s.si[t] = 0x7FFFFFFF;
+    }
+    __syncthreads();
     if (t < nsurv) {
       const float xt = s.sx[t];
       const int it = s.si[t];
-      int rank = 0;
-      for (int u = 0; u < nsurv; ++u) rank += beats(s.sx[u], s.si[u], xt, it);
+      const int rank = rank_among(s.sx, s.si, npad, xt, it);
       if (rank < K) {
         out_lp[rank] = xt - lse;
         out_tok[rank] = it;
@@ -450,12 +487,16 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
       }
     }
   }
+  const int kpad = (K + 15) & ~15;
+  if (t >= K && t < kpad) {
+    s.wx[t] = -INFINITY;
+    s.wi[t] = 0x7FFFFFFF;
+  }
   __syncthreads();
   if (t < K) {
     const float xt = s.wx[t];
     const int it = s.wi[t];
-    int rank = 0;
-    for (int u = 0; u < K; ++u) rank += beats(s.wx[u], s.wi[u], xt, it);
+    const int rank = rank_among(s.wx, s.wi, kpad, xt, it);
     out_lp[rank] = xt - lse;
     out_tok[rank] = it;
   }
