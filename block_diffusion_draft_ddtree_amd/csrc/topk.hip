@@ -73,106 +73,153 @@ __device__ __forceinline__ int rank_among(const float* xs, const int* is, int n,
   return rank;
 }
 
+// Radix-select histograms, three of them in rotation: pass p counts into
+// hist[p % 3] and clears hist[(p + 1) % 3] for the next pass. The bins are
+// then read by every wave (each finds the boundary digit itself), so a pass
+// needs one barrier: hist[(p + 1) % 3] was last read in pass p - 2, and
+// every wave has passed the barrier of pass p - 1, which follows that read.
 struct SelShared {
-  uint32_t hist[256];
+  uint32_t hist[3][256];
+  uint32_t kmax[16], kmin[16];  // per-wave key range of a bucket
+  uint32_t out_count;
+};
+
+// Zero the first two histograms (before pass 0; a barrier must follow).
+__device__ __forceinline__ void init_hists(SelShared& s) {
+  for (int i = threadIdx.x; i < 512; i += blockDim.x) (&s.hist[0][0])[i] = 0u;
+}
+__device__ __forceinline__ void clear_next(SelShared& s, int pass) {
+  uint32_t* h = s.hist[(pass + 1) % 3];
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) h[i] = 0u;
+}
+
+struct DigitSel {
   uint32_t digit;   // digit of the boundary bucket
   uint32_t need;    // how many to take from that bucket
   uint32_t above;   // active elements in buckets above it
   uint32_t in_bin;  // active elements in that bucket
-  uint32_t out_count;
 };
 
-__device__ __forceinline__ void zero_hist(SelShared& s) {
-  for (int i = threadIdx.x; i < 256; i += blockDim.x) s.hist[i] = 0u;
-}
-
-// With hist filled (and a barrier passed), find the bucket holding the
-// need-th largest active element. Ends with a barrier.
-__device__ void find_digit(SelShared& s, uint32_t need) {
-  if (threadIdx.x < 64) {
-    const int l = threadIdx.x;
-    const uint32_t h0 = s.hist[4 * l], h1 = s.hist[4 * l + 1];
-    const uint32_t h2 = s.hist[4 * l + 2], h3 = s.hist[4 * l + 3];
-    const uint32_t lsum = h0 + h1 + h2 + h3;
-    uint32_t suf = lsum;  // inclusive suffix sum over lanes (high digits last)
+// With hist filled (and a barrier passed), the bucket holding the need-th
+// largest counted element (need <= the total count). Computed by every wave
+// on its own; the result is wave-uniform.
+__device__ __forceinline__ DigitSel find_digit(const uint32_t* hist, uint32_t need) {
+  const int l = threadIdx.x & 63;
+  const uint32_t h0 = hist[4 * l], h1 = hist[4 * l + 1];
+  const uint32_t h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
+  const uint32_t lsum = h0 + h1 + h2 + h3;
+  uint32_t suf = lsum;  // inclusive suffix sum over lanes (high digits last)
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_down(suf, off, 64);
-      if (l + off < 64) suf += o;
-    }
-    const uint32_t above = suf - lsum;
-    if (above < need && need <= suf) {
-      uint32_t a = above, d, hh;
-      if (a + h3 >= need) {
-        d = 4 * l + 3; hh = h3;
-      } else if (a + h3 + h2 >= need) {
-        a += h3; d = 4 * l + 2; hh = h2;
-      } else if (a + h3 + h2 + h1 >= need) {
-        a += h3 + h2; d = 4 * l + 1; hh = h1;
-      } else {
-        a += h3 + h2 + h1; d = 4 * l; hh = h0;
-      }
-      s.digit = d;
-      s.above = a;
-      s.in_bin = hh;
-      s.need = need - a;
-    }
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_down(suf, off, 64);
+    if (l + off < 64) suf += o;
   }
-  __syncthreads();
+  const uint32_t above = suf - lsum;
+  const bool here = above < need && need <= suf;
+  uint32_t a = above, d, hh;
+  if (a + h3 >= need) {
+    d = 4 * l + 3; hh = h3;
+  } else if (a + h3 + h2 >= need) {
+    a += h3; d = 4 * l + 2; hh = h2;
+  } else if (a + h3 + h2 + h1 >= need) {
+    a += h3 + h2; d = 4 * l + 1; hh = h1;
+  } else {
+    a += h3 + h2 + h1; d = 4 * l; hh = h0;
+  }
+  const int src = __ffsll((unsigned long long)ddt::ballot(here)) - 1;
+  DigitSel r;
+  r.digit = (uint32_t)__shfl((int)d, src, 64);
+  r.above = (uint32_t)__shfl((int)a, src, 64);
+  r.in_bin = (uint32_t)__shfl((int)hh, src, 64);
+  r.need = need - r.above;
+  return r;
 }
 
 // Exact threshold inside the boundary bucket d0 of the relative digit:
 // elements of that bucket are taken iff (key > tkey) or (key == tkey and
 // ikey(index) >= tik), where ikey is larger for smaller indices. ACTIVE(i)
 // says whether element i is in the bucket; KEY(i), IKEY(i) give its keys.
-// All threads call this; ends with every thread holding the result.
+// Passes continue the rotation from pass number `pass` (whose histogram
+// is clear). All threads call this; every thread ends with the result.
 template <class Active, class Key, class IKey>
-__device__ __forceinline__ void refine_bucket(SelShared& sh, uint32_t need, int n_elems, int idx_passes,
-                              Active active, Key keyf, IKey ikeyf, uint32_t& tkey,
-                              uint32_t& tik) {
-  uint32_t prefix = 0u, mask = 0u, inb = 0u;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    __syncthreads();
-    zero_hist(sh);
-    __syncthreads();
+__device__ __forceinline__ void refine_bucket(SelShared& sh, uint32_t need, int n_elems,
+                                              int idx_passes, int pass, Active active, Key keyf,
+                                              IKey ikeyf, uint32_t& tkey, uint32_t& tik) {
+  // The bucket's keys share their high bits: find the highest bit where
+  // its largest and smallest keys differ and select digit by digit from
+  // there down (the shared bits would otherwise cost whole passes in which
+  // every element hits the same histogram bin).
+  uint32_t kx = 0u, kn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < n_elems; ++i) {
+    if (active(i)) {
+      const uint32_t k = keyf(i);
+      kx = k > kx ? k : kx;
+      kn = k < kn ? k : kn;
+    }
+  }
+  kx = ddt::wave_max_u32(kx);
+  kn = ~ddt::wave_max_u32(~kn);
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sh.kmax[wave] = kx;
+    sh.kmin[wave] = kn;
+  }
+  __syncthreads();
+  kx = 0u;
+  kn = 0xFFFFFFFFu;
+  for (int w = 0; w < nw; ++w) {
+    kx = sh.kmax[w] > kx ? sh.kmax[w] : kx;
+    kn = sh.kmin[w] < kn ? sh.kmin[w] : kn;
+  }
+  const uint32_t diff = kx ^ kn;
+  const int hb = diff ? 31 - __builtin_clz(diff) : -1;  // highest differing bit
+  const uint32_t low = hb >= 0 ? (uint32_t)((2ull << hb) - 1ull) : 0u;
+  uint32_t mask = ~low, prefix = kx & mask, inb = 0u;
+  bool counted = false;  // inb holds the bucket's count of keys == prefix
+  for (int top = hb; top >= 0; top -= 8, ++pass) {
+    const int shift = top >= 7 ? top - 7 : 0;
+    const uint32_t dmask = (uint32_t)((2ull << (top - shift)) - 1ull);
+    clear_next(sh, pass);
+    uint32_t* h = sh.hist[pass % 3];
 #pragma unroll
     for (int i = 0; i < n_elems; ++i) {
       if (active(i)) {
         const uint32_t k = keyf(i);
-        if ((k & mask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
+        if ((k & mask) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1u);
       }
     }
     __syncthreads();
-    find_digit(sh, need);
-    prefix |= sh.digit << shift;
-    mask |= 255u << shift;
-    need = sh.need;
-    inb = sh.in_bin;
+    const DigitSel ds = find_digit(h, need);
+    prefix |= ds.digit << shift;
+    mask |= dmask << shift;
+    need = ds.need;
+    inb = ds.in_bin;
+    counted = true;
   }
   tkey = prefix;
   tik = 0u;
+  if (!counted) inb = need + 1u;  // all keys equal: let the index decide
   if (need < inb) {
     uint32_t ip = 0u, im = 0u;
-    for (int shift = 8 * (idx_passes - 1); shift >= 0; shift -= 8) {
-      __syncthreads();
-      zero_hist(sh);
-      __syncthreads();
+    for (int shift = 8 * (idx_passes - 1); shift >= 0; shift -= 8, ++pass) {
+      clear_next(sh, pass);
+      uint32_t* h = sh.hist[pass % 3];
 #pragma unroll
       for (int i = 0; i < n_elems; ++i) {
         if (active(i) && keyf(i) == tkey) {
           const uint32_t ik = ikeyf(i);
-          if ((ik & im) == ip) atomicAdd(&sh.hist[(ik >> shift) & 255u], 1u);
+          if ((ik & im) == ip) atomicAdd(&h[(ik >> shift) & 255u], 1u);
         }
       }
       __syncthreads();
-      find_digit(sh, need);
-      ip |= sh.digit << shift;
+      const DigitSel ds = find_digit(h, need);
+      ip |= ds.digit << shift;
       im |= 255u << shift;
-      need = sh.need;
+      need = ds.need;
     }
     tik = ip;
   }
-  __syncthreads();
 }
 
 __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
@@ -193,7 +240,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
     const int e = t + kChunkThreads * j;
     x[j] = e < n ? src[e] : -INFINITY;
   }
-  zero_hist(sh);
+  init_hists(sh);
   if (t == 0) sh.out_count = 0u;
 
   float mx = -INFINITY;
@@ -209,7 +256,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
   for (int j = 0; j < kPerThread; ++j) {
     if (t + kChunkThreads * j < n) {
       s += __expf(x[j] - m);
-      atomicAdd(&sh.hist[rel_digit(m, x[j])], 1u);
+      atomicAdd(&sh.hist[0][rel_digit(m, x[j])], 1u);  // pass 0
     }
   }
   s = ddt::wave_reduce_uniform(s, ddt::OpSum());
@@ -217,15 +264,15 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
   __syncthreads();
 
   const uint32_t Kc = (uint32_t)min(K, n);
-  find_digit(sh, Kc);
-  const uint32_t d0 = sh.digit;
-  const uint32_t need = sh.need;
-  const bool loose = sh.above + sh.in_bin <= (uint32_t)cap;
-  const bool take_bin = loose || need == sh.in_bin;
+  const DigitSel ds0 = find_digit(sh.hist[0], Kc);
+  const uint32_t d0 = ds0.digit;
+  const uint32_t need = ds0.need;
+  const bool loose = ds0.above + ds0.in_bin <= (uint32_t)cap;
+  const bool take_bin = loose || need == ds0.in_bin;
   uint32_t tkey = 0u, tik = 0u;
   if (!take_bin) {
     refine_bucket(
-        sh, need, kPerThread, 2,
+        sh, need, kPerThread, 2, 1,
         [&](int j) { return t + kChunkThreads * j < n && rel_digit(m, x[j]) == d0; },
         [&](int j) { return ddt::f32_key(x[j]); },
         [&](int j) { return 0xFFFFu - (uint32_t)(t + kChunkThreads * j); }, tkey, tik);
@@ -442,22 +489,22 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   };
   const int per = (n_all + kMergeThreads - 1) / kMergeThreads;
 
-  zero_hist(s.sh);
+  init_hists(s.sh);
   __syncthreads();
-  for (int r = 0; r < per; ++r) {
+  for (int r = 0; r < per; ++r) {  // pass 0
     const int i = t + kMergeThreads * r;
-    if (i < n_all) atomicAdd(&s.sh.hist[rel_digit(M, elem_x(i))], 1u);
+    if (i < n_all) atomicAdd(&s.sh.hist[0][rel_digit(M, elem_x(i))], 1u);
   }
   __syncthreads();
-  find_digit(s.sh, (uint32_t)K);
-  const uint32_t d0 = s.sh.digit;
-  const uint32_t need = s.sh.need;
-  const bool take_bin = need == s.sh.in_bin;
+  const DigitSel ds0 = find_digit(s.sh.hist[0], (uint32_t)K);
+  const uint32_t d0 = ds0.digit;
+  const uint32_t need = ds0.need;
+  const bool take_bin = need == ds0.in_bin;
   uint32_t tkey = 0u, tik = 0u;
   const uint32_t idx_mask = idx_passes >= 4 ? 0xFFFFFFFFu : ((1u << (8 * idx_passes)) - 1u);
   if (!take_bin) {
     refine_bucket(
-        s.sh, need, per, idx_passes,
+        s.sh, need, per, idx_passes, 1,
         [&](int r) {
           const int i = t + kMergeThreads * r;
           return i < n_all && rel_digit(M, elem_x(i)) == d0;
