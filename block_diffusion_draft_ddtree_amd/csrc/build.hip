@@ -11,17 +11,21 @@
 // popping slot p's candidate creates node b, advances slot p to its next
 // sibling rank and opens slot b at child rank 0. So the frontier is an
 // array of at most B + 1 slots indexed by node id. Slot n lives in lane
-// n & 63, register n >> 6 of wave 0, which keeps everything about it in
-// registers: its candidate's order key and fp32 score, the candidate's
-// rank, the node's own score, depth, parent and rank, and the log-prob of
-// the candidate after the current one (prefetched from LDS so that
-// advancing a slot never waits on memory).
+// n & 63, register n >> 6 of wave 0, which keeps what a pop needs about it
+// in registers: its candidate's order key and fp32 score, the candidate's
+// rank and the node's depth (one word), the node's own score, and the
+// log-prob of the candidate after the current one (prefetched from LDS).
 //
-// A pop: each lane takes the max key over its slots, a DPP max inside each
-// 16-lane row plus four readlanes gives the wave max in a scalar register,
-// and a ballot finds the owner. Exact score ties fall back to a
-// wave-cooperative lexicographic comparison of the rank tuples, which are
-// rebuilt from parent/rank arrays kept in LDS.
+// A pop: each lane takes the max key over its slots; a DPP max inside each
+// 16-lane row, chained across rows by the two row broadcasts, leaves the
+// wave max in lane 63, and a ballot finds the owner. The owner's state is
+// read with one readlane per field, and the two slots that change are
+// written by selects on all lanes (no divergent branch). Each pop issues
+// two LDS reads for the log-probs its slots will need next and applies
+// them at the following pop, after that pop's reduction, so their latency
+// is off the serial chain. The new node's (parent, rank, depth) record is
+// one LDS word. Exact score ties fall back to a wave-cooperative
+// lexicographic comparison of the rank tuples, rebuilt from those records.
 //
 // Scores follow the fp32 left-to-right sum: a depth-1 candidate is logp[0][r]
 // itself, deeper ones fl(score(parent) + logp[d][r]).
@@ -32,11 +36,18 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxN = DDTREE_MAX_B + 1;
 
+// A node's record in one word: parent + 1 (11 bits), rank (10 bits), depth
+// (6 bits). The root is the all-zero word.
+__device__ __forceinline__ uint32_t pack_node(int parent, int rank, int depth) {
+  return (uint32_t)(parent + 1) | ((uint32_t)rank << 11) | ((uint32_t)depth << 21);
+}
+__device__ __forceinline__ int node_parent(uint32_t w) { return (int)(w & 2047u) - 1; }
+__device__ __forceinline__ int node_rank(uint32_t w) { return (int)((w >> 11) & 1023u); }
+__device__ __forceinline__ int node_depth(uint32_t w) { return (int)(w >> 21); }
+
 struct BuildLds {
   float lp[DDTREE_MAX_LK];
-  int16_t parent[kMaxN];
-  int16_t rank[kMaxN];
-  uint8_t depth[kMaxN];
+  uint32_t node[kMaxN + 64];  // node records; [kMaxN, kMaxN + 64) takes the other lanes' writes
 };
 
 // DPP controls (gfx9 encoding).
@@ -44,28 +55,22 @@ constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
 constexpr int kRowMirror = 0x140;      // lane i <-> 15 - i within each 16 lanes
+constexpr int kRowBcast15 = 0x142;     // lane 15 of each row -> the next row
+constexpr int kRowBcast31 = 0x143;     // lane 31 -> rows 2 and 3
 
-__device__ __forceinline__ uint32_t dpp_umax(uint32_t v, int ctrl_id) {
-  uint32_t o;
-  switch (ctrl_id) {
-    case 0: o = __builtin_amdgcn_update_dpp(v, v, kQuadXor1, 0xF, 0xF, false); break;
-    case 1: o = __builtin_amdgcn_update_dpp(v, v, kQuadXor2, 0xF, 0xF, false); break;
-    case 2: o = __builtin_amdgcn_update_dpp(v, v, kRowHalfMirror, 0xF, 0xF, false); break;
-    default: o = __builtin_amdgcn_update_dpp(v, v, kRowMirror, 0xF, 0xF, false); break;
-  }
-  return o > v ? o : v;
-}
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
-// Wave-wide max, returned in a scalar (uniform) register.
+// Wave-wide max of unsigned keys (0 is the identity), returned in a scalar
+// register: a max within each 16-lane row, then the rows are chained
+// through the row broadcasts so that lane 63 holds the max of all 64.
 __device__ __forceinline__ uint32_t wave_umax_uniform(uint32_t v) {
-  v = dpp_umax(v, 0);
-  v = dpp_umax(v, 1);
-  v = dpp_umax(v, 2);
-  v = dpp_umax(v, 3);  // every lane now holds the max of its 16-lane row
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
-  return ab > cd ? ab : cd;
+  v = umax(v, __builtin_amdgcn_update_dpp(0u, v, kQuadXor1, 0xF, 0xF, false));
+  v = umax(v, __builtin_amdgcn_update_dpp(0u, v, kQuadXor2, 0xF, 0xF, false));
+  v = umax(v, __builtin_amdgcn_update_dpp(0u, v, kRowHalfMirror, 0xF, 0xF, false));
+  v = umax(v, __builtin_amdgcn_update_dpp(0u, v, kRowMirror, 0xF, 0xF, false));
+  v = umax(v, __builtin_amdgcn_update_dpp(0u, v, kRowBcast15, 0xA, 0xF, false));
+  v = umax(v, __builtin_amdgcn_update_dpp(0u, v, kRowBcast31, 0xC, 0xF, false));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ float readlane_f(float x, int lane) {
@@ -74,15 +79,16 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
 
 // Rank at depth `d` (1-based) of the tuple of node `x` (depth(x) >= d).
 __device__ __forceinline__ int rank_at(const BuildLds& s, int x, int d) {
-  while (s.depth[x] > d) x = s.parent[x];
-  return s.rank[x];
+  uint32_t w = s.node[x];
+  while (node_depth(w) > d) w = s.node[node_parent(w)];
+  return node_rank(w);
 }
 
 // Wave-uniform: is candidate (slot a, rank ca) lexicographically before
 // candidate (slot b, rank cb)? Lane i holds element i of each rank tuple.
 __device__ bool cand_lex_less(const BuildLds& s, int a, int ca, int b, int cb) {
   const int lane = ddt::lane_id();
-  const int da = s.depth[a] + 1, db = s.depth[b] + 1;
+  const int da = node_depth(s.node[a]) + 1, db = node_depth(s.node[b]) + 1;
   int xa = -1, xb = -1;
   if (lane < da) xa = (lane == da - 1) ? ca : rank_at(s, a, lane + 1);
   if (lane < db) xb = (lane == db - 1) ? cb : rank_at(s, b, lane + 1);
@@ -94,24 +100,26 @@ __device__ bool cand_lex_less(const BuildLds& s, int a, int ca, int b, int cb) {
   return __shfl(xa, f, 64) < __shfl(xb, f, 64);
 }
 
+// The serial best-first pops, on wave 0. Every update is a select on all
+// lanes (no divergent branch), and the two log-prob prefetches of a pop (the popped slot's
+// sibling after next, the new slot's second child) are applied at the next
+// pop, after its reduction, so their LDS latency stays off the chain.
 template <int J>
 __device__ void pop_loop(BuildLds& s, int L, int K, int B) {
   const int lane = ddt::lane_id();
   // Per-slot state (slot n = lane + 64 * j).
-  uint32_t key[J];   // order key of the candidate's score, 0 = no candidate
-  float csc[J];      // candidate score
-  int crk[J];        // candidate rank
-  float nlp[J];      // log-prob of the following sibling candidate
-  float nsc[J];      // the node's own score
-  int dep[J];        // the node's depth
+  uint32_t key[J];  // order key of the candidate's score, 0 = no candidate
+  float csc[J];     // the candidate's score (the key merges -0 and +0)
+  uint32_t crd[J];  // candidate rank | node depth << 16
+  float nlp[J];     // log-prob of the candidate after the current one
+  float nsc[J];     // the node's own score
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     key[j] = 0u;
     csc[j] = 0.f;
-    crk[j] = 0;
+    crd[j] = 0u;
     nlp[j] = 0.f;
     nsc[j] = 0.f;
-    dep[j] = 0;
   }
   // Lane d (< L) holds logp[d][0]: the first child's log-prob at depth d + 1.
   const float row0 = lane < L ? s.lp[lane * K] : 0.f;
@@ -120,32 +128,35 @@ __device__ void pop_loop(BuildLds& s, int L, int K, int B) {
     key[0] = ddt::f32_key(csc[0]);
     nlp[0] = K > 1 ? s.lp[1] : 0.f;
   }
+  // Prefetches of the previous pop, not yet applied (lane -1: none).
+  int pf_pl = -1, pf_pj = 0, pf_bl = -1, pf_bj = 0;
+  float pf_pv = 0.f, pf_bv = 0.f;
 
   for (int b = 1; b <= B; ++b) {
-    uint32_t lk = 0u;
+    uint32_t lk = key[0];
     int lj = 0;
     bool ltie = false;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      if (key[j] > lk) {
-        lk = key[j];
-        lj = j;
-        ltie = false;
-      } else if (key[j] == lk && lk != 0u) {
-        ltie = true;
-      }
+    for (int j = 1; j < J; ++j) {
+      ltie = key[j] == lk ? (lk != 0u) : (key[j] > lk ? false : ltie);
+      lj = key[j] > lk ? j : lj;
+      lk = umax(lk, key[j]);
     }
     const uint32_t kmax = wave_umax_uniform(lk);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      nlp[j] = (lane == pf_pl && j == pf_pj) ? pf_pv : nlp[j];
+      nlp[j] = (lane == pf_bl && j == pf_bj) ? pf_bv : nlp[j];
+    }
     const uint64_t hit = ddt::ballot(lk == kmax);
     const uint64_t tie = ddt::ballot(lk == kmax && ltie);
-    int p;
+    int pl, pj;
     if (__popcll(hit) == 1 && tie == 0) {
-      const int wl = __ffsll((unsigned long long)hit) - 1;
-      p = wl + 64 * __builtin_amdgcn_readlane(lj, wl);
+      pl = __ffsll((unsigned long long)hit) - 1;
+      pj = __builtin_amdgcn_readlane(lj, pl);
     } else {
       // Several slots share the best score: smallest rank tuple wins.
-      p = -1;
-      int pc = 0;
+      int p = -1, pc = 0;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         uint64_t m = ddt::ballot(key[j] == kmax);
@@ -153,71 +164,68 @@ __device__ void pop_loop(BuildLds& s, int L, int K, int B) {
           const int l = __ffsll((unsigned long long)m) - 1;
           m &= m - 1;
           const int cand = l + 64 * j;
-          const int cc = __builtin_amdgcn_readlane(crk[j], l);
+          const int cc = (int)(__builtin_amdgcn_readlane(crd[j], l) & 0xFFFFu);
           if (p < 0 || cand_lex_less(s, cand, cc, p, pc)) {
             p = cand;
             pc = cc;
           }
         }
       }
+      p = __builtin_amdgcn_readfirstlane(p);
+      pl = p & 63;
+      pj = p >> 6;
     }
-    p = __builtin_amdgcn_readfirstlane(p);
-    const int pl = p & 63, pj = p >> 6;
-
     // Gather slot p's state from its owner lane.
-    int c = 0, dp = 0;
-    float sc = 0.f, nl = 0.f, ps = 0.f;
+    uint32_t cd = crd[0];
+    float nl = nlp[0], ps = nsc[0], sc = csc[0];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      if (j == pj) {
-        c = __builtin_amdgcn_readlane(crk[j], pl);
-        dp = __builtin_amdgcn_readlane(dep[j], pl);
-        sc = readlane_f(csc[j], pl);
-        nl = readlane_f(nlp[j], pl);
-        ps = readlane_f(nsc[j], pl);
-      }
+    for (int j = 1; j < J; ++j) {
+      cd = pj == j ? crd[j] : cd;
+      nl = pj == j ? nlp[j] : nl;
+      ps = pj == j ? nsc[j] : ps;
+      sc = pj == j ? csc[j] : sc;
     }
-    const int dn = dp + 1;
-    if (lane == 0) {
-      s.parent[b] = (int16_t)p;
-      s.rank[b] = (int16_t)c;
-      s.depth[b] = (uint8_t)dn;
-    }
-    // Advance slot p to its next sibling (rank c + 1, log-prob prefetched).
+    cd = __builtin_amdgcn_readlane(cd, pl);
+    nl = readlane_f(nl, pl);
+    ps = readlane_f(ps, pl);
+    sc = readlane_f(sc, pl);  // the popped candidate's score
+    const int c = (int)(cd & 0xFFFFu), dp = (int)(cd >> 16), dn = dp + 1;
+    const int p = pl + 64 * pj;
+    // Node b = (parent p, rank c, depth dn); lane 0 writes the record, the
+    // other lanes a spare word each.
+    s.node[lane == 0 ? b : kMaxN + lane] = pack_node(p, c, dn);
+    // Slot p advances to its next sibling (rank c + 1).
     const int c2 = c + 1;
-    float ps2 = 0.f;
     uint32_t pk = 0u;
+    float ps2 = 0.f;
     if (c2 < K) {
-      ps2 = (dp == 0) ? nl : (ps + nl);
+      ps2 = dp == 0 ? nl : ps + nl;
       pk = ddt::f32_key(ps2);
     }
-    const float nl2 = (c2 + 1 < K) ? s.lp[dp * K + c2 + 1] : 0.f;
-    // Open slot b at its first child.
+    const float nl2 = c2 + 1 < K ? s.lp[dp * K + c2 + 1] : 0.f;
+    // Slot b opens at its first child (rank 0 at depth dn + 1).
     uint32_t bk = 0u;
     float bs = 0.f;
     if (dn < L) {
       bs = sc + readlane_f(row0, dn);
       bk = ddt::f32_key(bs);
     }
-    const float bnl = (dn < L && K > 1) ? s.lp[dn * K + 1] : 0.f;
+    const float bnl = dn < L && K > 1 ? s.lp[dn * K + 1] : 0.f;
     const int bl = b & 63, bj = b >> 6;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      if (lane == pl && j == pj) {
-        key[j] = pk;
-        csc[j] = ps2;
-        crk[j] = c2;
-        nlp[j] = nl2;
-      }
-      if (lane == bl && j == bj) {
-        key[j] = bk;
-        csc[j] = bs;
-        crk[j] = 0;
-        nlp[j] = bnl;
-        nsc[j] = sc;
-        dep[j] = dn;
-      }
+      const bool isp = lane == pl && j == pj, isb = lane == bl && j == bj;
+      key[j] = isb ? bk : (isp ? pk : key[j]);
+      csc[j] = isb ? bs : (isp ? ps2 : csc[j]);
+      crd[j] = isb ? ((uint32_t)dn << 16) : (isp ? ((uint32_t)c2 | ((uint32_t)dp << 16)) : crd[j]);
+      nsc[j] = isb ? sc : nsc[j];
     }
+    pf_pl = pl;
+    pf_pj = pj;
+    pf_pv = nl2;
+    pf_bl = bl;
+    pf_bj = bj;
+    pf_bv = bnl;
   }
   // Node scores to LDS (the lp table is no longer needed; reuse its space).
   float* score_out = s.lp;
@@ -238,11 +246,7 @@ __global__ __launch_bounds__(kThreads) void build_kernel(
   const int t = threadIdx.x;
   const int LK = L * K;
   for (int i = t; i < LK; i += kThreads) s.lp[i] = logp[i];
-  if (t == 0) {
-    s.parent[0] = -1;
-    s.rank[0] = 0;
-    s.depth[0] = 0;
-  }
+  if (t == 0) s.node[0] = 0u;  // the root
   __syncthreads();
   if (t < 64) pop_loop<J>(s, L, K, B);
   __syncthreads();
@@ -250,10 +254,11 @@ __global__ __launch_bounds__(kThreads) void build_kernel(
   const int N = B + 1;
   const float* nscore = s.lp;
   for (int n = t; n < N; n += kThreads) {
-    const int d = s.depth[n];
-    parent_out[n] = s.parent[n];
+    const uint32_t rec = s.node[n];
+    const int d = node_depth(rec);
+    parent_out[n] = node_parent(rec);
     depth_out[n] = d;
-    tok_out[n] = n == 0 ? *root_token : token[(d - 1) * K + s.rank[n]];
+    tok_out[n] = n == 0 ? *root_token : token[(d - 1) * K + node_rank(rec)];
     if (score_out) score_out[n] = nscore[n];
     // Ancestor-or-self row, written from the high word down.
     uint32_t* row = anc + (int64_t)n * W;
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void build_kernel(
     const int wn = n >> 5;
     for (; wcur > wn; --wcur) row[wcur] = 0u;
     uint32_t acc = 0u;
-    for (int j = n; j != -1; j = s.parent[j]) {
+    for (int j = n; j != -1; j = node_parent(s.node[j])) {
       const int wj = j >> 5;
       while (wj < wcur) {
         row[wcur] = acc;
