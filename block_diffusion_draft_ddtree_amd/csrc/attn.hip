@@ -535,13 +535,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   PBlock pb;  // weights of the previous block
   auto step = [&](int sb, bool first, const char* kc, char* kn, char* vdst, const char* vprev) {
     const int key0 = (sb * kStreams + st) * kBK;
-    const f32x16 sacc = block_qk<D>(kc + soff, qf, lane);
-    // The copies enter the texture-address unit at 64 B per clock, and a
-    // wave whose copies are queued there cannot issue further; so they are
-    // spread over the step: K once the Q.K products are under way, V
-    // between the score reduction and the products.
-    __builtin_amdgcn_sched_barrier(0);
+    // The copies enter the texture-address unit at about 45 B per clock per
+    // CU, and a wave whose copies are queued there cannot issue further; so
+    // they are spread over the step: K first, V between the score
+    // reduction and the products.
     if (sb + 1 < sb1) copy_k(sb + 1, kn);
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x16 sacc = block_qk<D>(kc + soff, qf, lane);
     __builtin_amdgcn_sched_barrier(0);
     auto mid = [&]() { copy_v(sb, vdst); };
     const bool masked = key0 + kBK > S;
@@ -569,19 +569,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   block_pv<D>(((sb1 - 1 - sb0) & 1 ? v1 : v0) + soff, vl, pb, o, lsum);
   __syncthreads();
 
-  // Merge the four streams. Every wave parks its fp32 output tile and its
-  // (reference max, sum) in LDS; then the wave of stream s merges the
-  // 32-dim output tile dt = s of its rows over the streams.
+  // Merge the four streams. Every wave parks its (reference max, sum) and
+  // the fp32 output tiles it does not merge itself in LDS; then the wave of
+  // stream s merges the 32-dim output tile dt = s of its rows over the
+  // streams, its own share straight from registers.
   const float l_tot = lsum[0];
   {
     char* mine = (st == 0 ? k0 : st == 1 ? v0 : st == 2 ? k1 : v1) + rw * C::OB;
     float4* ob = reinterpret_cast<float4*>(mine);
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+    for (int dt = 0; dt < C::DT; ++dt) {
+      if (dt == st) continue;
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd)
         ob[(dt * 4 + qd) * 64 + lane] =
             make_float4(o[dt][4 * qd], o[dt][4 * qd + 1], o[dt][4 * qd + 2], o[dt][4 * qd + 3]);
+    }
     mlx[wave * 64 + lane] = make_float2(m_run, l_tot);
   }
   __syncthreads();
@@ -605,6 +608,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int s = 0; s < kStreams; ++s) {
     const float w = __builtin_amdgcn_exp2f(ms[s] - Mu);
     L += w * ls[s];
+    if (s == st) {
+#pragma unroll
+      for (int d = 0; d < C::DT; ++d)
+        if (d == st) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] += w * o[d][r];
+        }
+      continue;
+    }
     const char* src = (s == 0 ? k0 : s == 1 ? v0 : s == 2 ? k1 : v1) + rw * C::OB;
     const float4* ob = reinterpret_cast<const float4*>(src);
 #pragma unroll
