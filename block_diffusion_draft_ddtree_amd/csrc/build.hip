@@ -73,6 +73,23 @@ __device__ __forceinline__ uint32_t wave_umax_uniform(uint32_t v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+constexpr int kRowShr1 = 0x111;        // lane i <- lane i - n within each row
+constexpr int kRowShr2 = 0x112;
+constexpr int kRowShr4 = 0x114;
+constexpr int kRowShr8 = 0x118;
+constexpr int kWaveShr1 = 0x138;       // lane i <- lane i - 1 across the wave
+
+// Inclusive prefix max over lanes (shifts 1, 2, 4, 8 within each row, then
+// the row broadcasts across rows).
+__device__ __forceinline__ uint32_t wave_incl_umax_scan(uint32_t v) {
+  v = umax(v, __builtin_amdgcn_update_dpp(0u, v, kRowShr1, 0xF, 0xF, false));
+  v = umax(v, __builtin_amdgcn_update_dpp(0u, v, kRowShr2, 0xF, 0xF, false));
+  v = umax(v, __builtin_amdgcn_update_dpp(0u, v, kRowShr4, 0xF, 0xF, false));
+  v = umax(v, __builtin_amdgcn_update_dpp(0u, v, kRowShr8, 0xF, 0xF, false));
+  v = umax(v, __builtin_amdgcn_update_dpp(0u, v, kRowBcast15, 0xA, 0xF, false));
+  return umax(v, __builtin_amdgcn_update_dpp(0u, v, kRowBcast31, 0xC, 0xF, false));
+}
+
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), lane));
 }
@@ -123,16 +140,63 @@ __device__ void pop_loop(BuildLds& s, int L, int K, int B) {
   }
   // Lane d (< L) holds logp[d][0]: the first child's log-prob at depth d + 1.
   const float row0 = lane < L ? s.lp[lane * K] : 0.f;
-  if (lane == 0) {
-    csc[0] = s.lp[0];
-    key[0] = ddt::f32_key(csc[0]);
-    nlp[0] = K > 1 ? s.lp[1] : 0.f;
+  // Root run. The first pops take the root's children in rank order for as
+  // long as each beats every first child opened before it (the only other
+  // candidates): exactly what the serial pops below would do, a tie
+  // included (it stops the run and the loop resolves it). A wave handles 63
+  // ranks at once: lane i holds rank c + i, a prefix max over the lanes
+  // gives the best child opened before it, and the first lane that fails
+  // ends the run. Nodes are numbered in rank order, as the pops number them.
+  int b = 1, c = 0;
+  {
+    uint32_t M = 0u;  // best first-child key opened so far
+    const float lc = L > 1 ? readlane_f(row0, 1) : 0.f;
+    const float nl1 = L > 1 && K > 1 ? s.lp[K + 1] : 0.f;
+    while (b <= B && c < K) {
+      const int rcap = min(min(K - c, B - b + 1), 63);
+      const float si = s.lp[min(c + lane, K - 1)];  // score of rank c + lane
+      const uint32_t ki = ddt::f32_key(si);
+      const float ci = si + lc;                     // its first child's score
+      const uint32_t ui = L > 1 ? ddt::f32_key(ci) : 0u;
+      const uint32_t incl = umax(M, wave_incl_umax_scan(ui));
+      const uint32_t excl = umax(M, __builtin_amdgcn_update_dpp(0u, incl, kWaveShr1, 0xF, 0xF, false));
+      const bool ok = lane < rcap && ki > (lane == 0 ? M : excl);
+      const uint64_t fail = ddt::ballot(!ok);  // never empty: lane rcap fails
+      const int R = __ffsll((unsigned long long)fail) - 1;
+      if (R == 0) break;
+      s.node[lane < R ? b + lane : kMaxN + lane] = pack_node(0, c + lane, 1);
+      // Run element i goes to the lane of slot b + i.
+      const int from = ((lane - b) & 63) * 4;
+      const uint32_t km = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)ui);
+      const float cm = __int_as_float(__builtin_amdgcn_ds_bpermute(from, __float_as_int(ci)));
+      const float sm = __int_as_float(__builtin_amdgcn_ds_bpermute(from, __float_as_int(si)));
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int n = lane + 64 * j;
+        const bool inr = n >= b && n < b + R;
+        key[j] = inr ? km : key[j];
+        csc[j] = inr ? cm : csc[j];
+        crd[j] = inr ? (1u << 16) : crd[j];
+        nsc[j] = inr ? sm : nsc[j];
+        nlp[j] = inr ? nl1 : nlp[j];
+      }
+      M = __builtin_amdgcn_readlane(incl, R - 1);
+      b += R;
+      c += R;
+      if (R < rcap) break;
+    }
   }
   // Prefetches of the previous pop, not yet applied (lane -1: none).
   int pf_pl = -1, pf_pj = 0, pf_bl = -1, pf_bj = 0;
   float pf_pv = 0.f, pf_bv = 0.f;
-
-  for (int b = 1; b <= B; ++b) {
+  // The root slot's candidate is now rank c.
+  if (lane == 0) {
+    csc[0] = c < K ? s.lp[c] : 0.f;
+    key[0] = c < K ? ddt::f32_key(csc[0]) : 0u;
+    crd[0] = (uint32_t)c;
+    nlp[0] = c + 1 < K ? s.lp[c + 1] : 0.f;
+  }
+  for (; b <= B; ++b) {
     uint32_t lk = key[0];
     int lj = 0;
     bool ltie = false;

@@ -83,6 +83,35 @@ def test_deep_trees(B):
     assert ref.depth.max() >= 5
 
 
+@pytest.mark.parametrize("ties", [False, True])
+@pytest.mark.parametrize("B", [63, 64, 130, 200, 290])
+def test_wide_root_runs(ties, B):
+    """A flat first position: the root's children pop in runs longer than a
+    wave (63 ranks per step) until a first child or an exact tie interrupts
+    them; the order must match the serial best-first pops bit for bit."""
+    g = synth.rng("test", 640 + B, int(ties))
+    L, K = 4, 300
+    first = np.linspace(0.0, -3.0, K, dtype=np.float32)
+    if ties:
+        first = np.round(first * 8.0) / 8.0  # runs of equal log-probs
+    lp = np.empty((L, K), dtype=np.float32)
+    lp[0] = first
+    for d in range(1, L):  # every step below the root costs at least 1.5
+        lp[d] = np.float32(-1.5) - np.sort(np.abs(g.standard_normal(K)).astype(np.float32))
+    lp[1, 0] = np.float32(-1.5)  # a first child ties a root child in the ties case
+    tok = np.stack([g.choice(100000, size=K, replace=False) for _ in range(L)]).astype(np.int32)
+    ref = _compare(lp, tok, B, twice=True)
+    assert (ref.depth == 1).sum() >= min(B, 100)
+
+
+def test_root_run_one_position():
+    """L = 1: the whole tree is the root's first B children."""
+    g = synth.rng("test", 650, 0)
+    lp, tok = synth.sorted_logp_table(1, 200, 1000, g)
+    ref = _compare(lp, tok, 150)
+    assert ref.parent.tolist() == [-1] + [0] * 150
+
+
 def test_special_cases():
     g = synth.rng("test", 620, 0)
     lp, tok = synth.sorted_logp_table(16, 1, 1000, g)
