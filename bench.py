@@ -109,8 +109,8 @@ def compact_bytes(w, a: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the hot path runs on a single MI355X "
-              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the hot path runs on a single MI355X; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
