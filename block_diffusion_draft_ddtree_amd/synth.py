@@ -242,6 +242,18 @@ def sorted_logp_table(L: int, K: int, V: int, g: np.random.Generator,
     return np.ascontiguousarray(vals, dtype=np.float32), tok
 
 
+def target_logits(g: np.random.Generator, N: int, V: int, peaks=None,
+                  boost: float = 8.0) -> tuple[np.ndarray, np.ndarray]:
+    """The verifier head's logits for N tree nodes, bf16 [N, V]: 2 N(0,1)
+    rounded to bf16, plus `boost` at peaks[n] when given (the token the
+    target prefers after node n). Returns (uint16 bits, equal fp32 values)."""
+    x = 2.0 * g.standard_normal((N, V), dtype=np.float32)
+    if peaks is not None:
+        x[np.arange(N), np.asarray(peaks)] += np.float32(boost)
+    bits = f32_to_bf16_bits(x)
+    return bits, bf16_bits_to_f32(bits)
+
+
 # ----------------------------------------------------------------------------
 # Attention tensors
 # ----------------------------------------------------------------------------

@@ -1,4 +1,5 @@
-"""Oracle: the greedy accept walk and the KV-cache compaction of a round.
+"""Oracle: the target's greedy choice per node, the greedy accept walk and
+the KV-cache compaction of a round.
 
 Test infrastructure only (see the package docstring).
 
@@ -18,7 +19,11 @@ Sources
 
 Readings where the pages are silent
 -----------------------------------
-* Greedy only: ``target_argmax[n]`` is the target's argmax after node n.
+* Greedy only: ``target_argmax[n]`` is the target's argmax after node n,
+  taken over the V logits the verifier's head gives node n: the largest
+  value compared as fp32 (bf16 logits widen exactly; -0 equals +0, -inf is
+  allowed, NaN is not), the smallest token id among equal maxima (the same
+  tie rule as the top-K rank order).
 * The walk is computed here by path consistency rather than by descending:
   node n is consistent iff every edge p -> c on the root-to-n path has
   token[c] == target_argmax[p]. Siblings carry distinct tokens, so the
@@ -33,6 +38,19 @@ Readings where the pages are silent
 from __future__ import annotations
 
 import numpy as np
+
+
+def target_argmax(logits) -> np.ndarray:
+    """int32 [N]: for each row, the first index holding the row's maximum."""
+    x = np.asarray(logits, dtype=np.float32)
+    if x.ndim != 2 or x.shape[1] < 1:
+        raise ValueError("logits must be [N, V] with V >= 1")
+    if np.isnan(x).any():
+        raise ValueError("NaN logits")
+    out = np.empty(x.shape[0], dtype=np.int32)
+    for n in range(x.shape[0]):
+        out[n] = int(np.flatnonzero(x[n] == x[n].max())[0])
+    return out
 
 
 def accept_walk(parent, node_token, target_argmax, L: int):

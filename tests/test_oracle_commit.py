@@ -1,8 +1,10 @@
-"""Pins for the oracle's accept walk and KV compaction (CPU only).
+"""Pins for the oracle's target argmax, accept walk and KV compaction (CPU
+only).
 
-Walk: "DDTree Deep Dive" page, section 6 (descend into the child matching the
-target's token; the first unmatched token becomes the bonus). Compaction:
-section 5 (keep only the accepted path, gathered in place)."""
+Argmax and walk: "DDTree Deep Dive" page, section 6 (the target's greedy
+choice after each node; descend into the child matching it; the first
+unmatched token becomes the bonus). Compaction: section 5 (keep only the
+accepted path, gathered in place)."""
 import numpy as np
 import pytest
 
@@ -94,3 +96,50 @@ def test_compaction_patterns():
         np.testing.assert_array_equal(out, inplace)
         for k in range(1, a + 1):
             np.testing.assert_array_equal(out[..., S + k, :], kv[..., S + acc[k], :])
+
+
+# ---------------------------------------------------------------------------
+# target argmax
+# ---------------------------------------------------------------------------
+
+def test_argmax_hand_cases():
+    ninf = -np.inf
+    rows = [
+        ([1.0, 3.0, 3.0, 2.0], 1),          # equal maxima: the smaller id
+        ([ninf, ninf, ninf], 0),            # a fully masked row
+        ([-0.0, 0.0, -1.0], 0),             # -0 and +0 are equal maxima
+        ([0.0, -0.0, 1e-45], 2),            # a denormal beats both zeros
+        ([-5.0, ninf, -4.0, -4.0], 2),
+        ([7.0], 0),
+    ]
+    for vals, want in rows:
+        got = oc.target_argmax(np.array([vals], dtype=np.float32))
+        assert got.tolist() == [want], (vals, got)
+
+
+def test_argmax_matches_sort_order():
+    """Independent route: rank every token by (value desc, id asc) with a
+    lexicographic sort and take the first; rows carry many exact ties."""
+    g = synth.rng("test", 660, 0)
+    x = np.round(g.standard_normal((40, 3001)).astype(np.float32) * 2.0) / 2.0
+    x[5] = -np.inf
+    x[6, 17] = np.inf
+    got = oc.target_argmax(x)
+    for n in range(x.shape[0]):
+        order = np.lexsort((np.arange(x.shape[1]), -x[n].astype(np.float64)))
+        assert got[n] == order[0]
+        assert np.all(x[n, : got[n]] < x[n, got[n]])   # nothing earlier ties it
+        assert np.all(x[n] <= x[n, got[n]])
+
+
+def test_argmax_bf16_rows_widen_exactly():
+    g = synth.rng("test", 661, 0)
+    bits, vals = synth.normal_bf16(g, (8, 999))
+    widened = (bits.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(widened, vals)
+    assert np.array_equal(oc.target_argmax(vals), oc.target_argmax(widened))
+
+
+def test_argmax_rejects_nan():
+    with pytest.raises(ValueError):
+        oc.target_argmax(np.array([[1.0, np.nan]], dtype=np.float32))
