@@ -32,6 +32,7 @@ MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 ATTN_SOURCE = os.path.join(ROOT, "block_diffusion_draft_ddtree_amd", "csrc", "attn.hip")
 COPY_PROBE_BYTES = 256 << 20  # bytes read and bytes written by the copy probe
+SPIN_CYCLES = 10_000_000      # ~5 ms of device spin ahead of each stage's timed reps
 
 
 def traffic_summary_path(workload: str) -> str:
@@ -102,6 +103,11 @@ def topk_bytes(w):
     return 4 * w.L * w.V + 8 * w.L * w.K
 
 
+def argmax_bytes(w):
+    """ddtree_target_argmax: the bf16 [N, V] logits once, the int32 [N] ids."""
+    return 2 * w.N * w.V + 4 * w.N
+
+
 def compact_bytes(w, a: int):
     return 8 * a * w.layers * w.Hkv * w.D
 
@@ -151,6 +157,11 @@ def main():
     tgt_np = synth.target_argmax_follow_peak(depth, lg.peak, w.L, w.V,
                                              synth.rng(w.family, 0, synth.STREAM_TARGET))
     tgt = torch.from_numpy(tgt_np).to(dev)
+    # Target head logits per node whose argmax is that same token (a boost
+    # well above the largest of 152k normal draws), for the argmax stage.
+    tl_bits, _ = synth.target_logits(synth.rng(w.family, 0, synth.STREAM_TARGET_LOGITS), w.N, w.V,
+                                     peaks=tgt_np, boost=40.0)
+    tlog = torch.from_numpy(tl_bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -202,9 +213,12 @@ def main():
     R = args.stage_reps
 
     def timed(fn, reps):
+        # A spin kernel ahead of the reps keeps the device busy while the
+        # host enqueues them, so the events see device time, not Python's.
         a, b = ev(), ev()
         fn()
         torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
         a.record(stream)
         for i in range(reps):
             fn(i)
@@ -218,6 +232,8 @@ def main():
     stage["tree_attn"] = timed(lambda i=0: rnd.attn(i % w.layers, q, kv, w.S), max(R, 2 * w.layers))
     stage["walk"] = timed(lambda i=0: rnd.walk(tgt), R)
     stage["kv_compact"] = timed(lambda i=0: rnd.compact(kv, w.S), R)
+    stage["target_argmax"] = timed(lambda i=0: rnd.target_argmax(tlog), R)
+    argmax_ok = bool(torch.equal(rnd.target_choice, tgt))
     if graph is None:
         attn_live = [a.elapsed_time(b) * 1e3 / w.layers for a, b in attn_pairs]
         attn_us = float(np.mean(attn_live))
@@ -266,6 +282,8 @@ def main():
         "round_wall_us": round(wall_us, 2),
         "stage_us": {k: round(v, 3) for k, v in stage.items()},
         "topk_TBps": round(topk_bytes(w) / (stage["topk"] * 1e-6) / 1e12, 3),
+        "target_argmax_TBps": round(argmax_bytes(w) / (stage["target_argmax"] * 1e-6) / 1e12, 3),
+        "target_argmax_matches": argmax_ok,
         "accepted": a_acc,
         "depth_hist": np.bincount(depth).tolist(),
         "roofline": roof,

@@ -23,6 +23,7 @@ DDTREE_ERR_WORKSPACE_TOO_SMALL = 3
 DDTREE_ERR_HIP = 4
 
 MAX_L, MAX_K, MAX_B, MAX_LK = 32, 1024, 1024, 32768
+DDTREE_DTYPE_F32, DDTREE_DTYPE_BF16 = 0, 1
 
 _lib = None
 _vp, _i32, _i64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
@@ -37,6 +38,8 @@ _SIGNATURES = {
     "ddtree_tree_attn_workspace_bytes": (_i32, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "ddtree_tree_attn": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                 _i32, _vp, _vp, _sz, _vp]),
+    "ddtree_target_argmax_workspace_bytes": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "ddtree_target_argmax": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
     "ddtree_accept_walk": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "ddtree_kv_compact": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
 }
@@ -108,6 +111,13 @@ def ddtree_tree_attn_workspace_bytes(N: int, Hq: int, Hkv: int, D: int, S: int) 
     return out.value
 
 
+def ddtree_target_argmax_workspace_bytes(dtype: int, N: int, V: int) -> int:
+    out = _sz(0)
+    _check(lib().ddtree_target_argmax_workspace_bytes(dtype, N, V, ctypes.byref(out)),
+           "ddtree_target_argmax_workspace_bytes")
+    return out.value
+
+
 def workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
@@ -174,6 +184,27 @@ def ddtree_tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: int,
         S, S_cap, N, Hq, Hkv, D, scale, _dev(anc, anc.dtype, "anc"), anc.shape[1],
         _dev(out, torch.bfloat16, "out"), _dev(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream)), "ddtree_tree_attn")
+    return out
+
+
+def ddtree_target_argmax(logits: torch.Tensor, out=None, ws=None, stream=None) -> torch.Tensor:
+    """fp32 or bf16 logits [N, V] (row stride may exceed V) -> int32 [N] on the device.
+
+    ws: a uint8 device tensor of at least ddtree_target_argmax_workspace_bytes()
+    bytes (allocated when None)."""
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [N, V] with unit column stride")
+    if not logits.is_cuda or logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be a float32 or bfloat16 device tensor")
+    N, V = logits.shape
+    dtype = DDTREE_DTYPE_BF16 if logits.dtype == torch.bfloat16 else DDTREE_DTYPE_F32
+    if ws is None:
+        ws = workspace(ddtree_target_argmax_workspace_bytes(dtype, N, V), logits.device)
+    out = torch.empty(N, dtype=torch.int32, device=logits.device) if out is None else out
+    _check(lib().ddtree_target_argmax(logits.data_ptr(), dtype, logits.stride(0), N, V,
+                                      _dev(out, torch.int32, "out"), ws.data_ptr(), ws.numel(),
+                                      _stream(stream)),
+           "ddtree_target_argmax")
     return out
 
 

@@ -118,6 +118,37 @@ DDT_API int ddtree_tree_attn(const uint16_t* q, const uint16_t* k, const uint16_
                                stream);
 }
 
+static int argmax_check(int dtype, int N, int V) {
+  if (N < 1 || V < 1) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (dtype != DDTREE_DTYPE_F32 && dtype != DDTREE_DTYPE_BF16) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (N > DDTREE_MAX_B + 1 || V > DDTREE_MAX_V) return DDTREE_ERR_UNSUPPORTED;
+  return DDTREE_OK;
+}
+
+DDT_API int ddtree_target_argmax_workspace_bytes(int dtype, int N, int V, size_t* bytes) {
+  if (!bytes) return DDTREE_ERR_INVALID_ARGUMENT;
+  const int st = argmax_check(dtype, N, V);
+  if (st) return st;
+  *bytes = ddt_host::argmax_workspace_bytes(N, V, dtype == DDTREE_DTYPE_BF16 ? 2 : 4);
+  return DDTREE_OK;
+}
+
+DDT_API int ddtree_target_argmax(const void* logits, int dtype, int64_t row_stride, int N,
+                                 int V, int32_t* out, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  const int st = argmax_check(dtype, N, V);
+  if (st) return st;
+  if (!logits || !out || !ws) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (row_stride < V) return DDTREE_ERR_INVALID_ARGUMENT;
+  const uintptr_t esize = dtype == DDTREE_DTYPE_BF16 ? 2u : 4u;
+  if (reinterpret_cast<uintptr_t>(logits) % esize != 0) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(ws) % 8 != 0) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < ddt_host::argmax_workspace_bytes(N, V, (int)esize))
+    return DDTREE_ERR_WORKSPACE_TOO_SMALL;
+  return ddt_host::argmax_launch(logits, dtype == DDTREE_DTYPE_BF16, row_stride, N, V, ws, out,
+                                 stream);
+}
+
 DDT_API int ddtree_accept_walk(const int32_t* parent, const int32_t* node_token, int N, int L,
                                const int32_t* target_argmax, int32_t* acc, int32_t* n_acc,
                                int32_t* next_bonus, hipStream_t stream) {

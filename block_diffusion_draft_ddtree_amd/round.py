@@ -1,7 +1,8 @@
 """One DDTree decode round on the device: topk -> build -> tree attention per
-layer -> accept walk -> KV compaction ("DDTree Deep Dive", section 3: the
-draft, tree_build, tree_compile, verify, commit stages; the drafter forward
-and the target's non-attention layers are outside this library).
+layer -> (target argmax) -> accept walk -> KV compaction ("DDTree Deep
+Dive", section 3: the draft, tree_build, tree_compile, verify, commit
+stages; the drafter forward and the target's non-attention layers, LM head
+included, are outside this library).
 
 All buffers are allocated once (torch device memory) so a round enqueues
 only libddtree kernels, which also makes the round capturable in a HIP
@@ -54,6 +55,9 @@ class DraftTreeRound:
         self.anc = torch.empty((s.N, s.W), **i32)
         self.attn_out = torch.empty((s.layers, s.N, s.Hq, s.D), dtype=torch.bfloat16, device=dev)
         self.ws_attn = bd.workspace(bd.ddtree_tree_attn_workspace_bytes(s.N, s.Hq, s.Hkv, s.D, S_max), dev)
+        self.target_choice = torch.empty(s.N, **i32)
+        self.ws_argmax = bd.workspace(
+            bd.ddtree_target_argmax_workspace_bytes(bd.DDTREE_DTYPE_BF16, s.N, s.V), dev)
         self.acc = torch.empty(s.L + 1, **i32)
         self.n_acc = torch.empty(1, **i32)
         self.next_bonus = torch.empty(1, **i32)
@@ -68,6 +72,10 @@ class DraftTreeRound:
     def attn(self, layer: int, q, kv, S: int):
         bd.ddtree_tree_attn(q[layer], kv[layer, 0], kv[layer, 1], S, self.anc,
                             out=self.attn_out[layer], ws=self.ws_attn)
+
+    def target_argmax(self, target_logits):
+        """bf16 [N, V] target head logits -> the target's greedy token per node."""
+        return bd.ddtree_target_argmax(target_logits, out=self.target_choice, ws=self.ws_argmax)
 
     def walk(self, target_argmax):
         bd.ddtree_accept_walk(self.parent, self.node_token, self.shape.L, target_argmax,

@@ -26,6 +26,7 @@ STREAM_QKV = 1
 STREAM_TARGET = 2
 STREAM_ACCEPT = 3
 STREAM_EXTRA = 4
+STREAM_TARGET_LOGITS = 5
 
 WORKLOAD_IDS = {
     "tiny": 1,

@@ -6,6 +6,7 @@
  *   ddtree_topk         log-softmax + top-K of the drafter's per-position logits
  *   ddtree_build        best-first top-B prefix tree, node arrays, ancestor mask
  *   ddtree_tree_attn    ancestor-only GQA attention of the tree nodes (per layer)
+ *   ddtree_target_argmax  the target's greedy token after every tree node
  *   ddtree_accept_walk  greedy walk of the target's argmax down the tree
  *   ddtree_kv_compact   in-place gather of the accepted path's K/V rows
  *
@@ -52,6 +53,10 @@ typedef enum ddtree_status {
   DDTREE_ERR_WORKSPACE_TOO_SMALL = 3,/* ws_bytes below the queried size        */
   DDTREE_ERR_HIP = 4                 /* a HIP launch or runtime call failed    */
 } ddtree_status;
+
+/* Element types of ddtree_target_argmax's logits. */
+#define DDTREE_DTYPE_F32 0
+#define DDTREE_DTYPE_BF16 1
 
 /* Limits checked by the calls below. */
 #define DDTREE_MAX_L 32        /* drafted block positions (the pages use 16) */
@@ -157,6 +162,35 @@ int ddtree_tree_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      float scale, const uint32_t* anc, int mask_words,
                      uint16_t* out, void* ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * ddtree_target_argmax -- the target's greedy choice after every tree node.
+ *
+ * Source: [DD] section 6 (the walk compares each node's drafted children
+ * with the token the target picks after that node; at temperature 0 the
+ * pick is the argmax of the target head's logits for the node); [AH] Core
+ * Mechanism (one target pass scores every node).
+ *
+ * logits      [N, row_stride] elements of type `dtype` (DDTREE_DTYPE_F32:
+ *             float; DDTREE_DTYPE_BF16: uint16_t bfloat16 bits); row n holds
+ *             the V logits of node n. Aligned to the element size; NaN is
+ *             not allowed (the result is then unspecified), -inf is.
+ * row_stride  elements between rows, >= V.
+ * N, V        1 <= N <= DDTREE_MAX_B + 1, 1 <= V <= DDTREE_MAX_V.
+ * out         out int32 [N]: out[n] = the smallest v with logits[n][v] equal
+ *             to the row's maximum, compared as fp32 (bf16 widens exactly;
+ *             -0 equals +0). It is the target_argmax of ddtree_accept_walk.
+ *
+ * ws/ws_bytes device scratch of at least ddtree_target_argmax_workspace_bytes()
+ *             bytes (N * S * 8 with S <= 32 chunks per row), 8-byte aligned;
+ *             no state is kept in it between calls.
+ *
+ * One streaming pass over N * V elements, each row split over S workgroups
+ * whose bests a second small kernel combines.
+ * ---------------------------------------------------------------------- */
+int ddtree_target_argmax_workspace_bytes(int dtype, int N, int V, size_t* bytes /* host */);
+int ddtree_target_argmax(const void* logits, int dtype, int64_t row_stride, int N, int V,
+                         int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * ddtree_accept_walk -- greedy verification walk down the tree.

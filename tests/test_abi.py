@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(bd.EXPORTS)
@@ -109,3 +109,26 @@ def test_walk_and_compact_validation(lib):
     assert c(P(FAKE), 48, 4, 4160, 128, 4096, 65, 16, P(FAKE), P(FAKE), None) == bd.DDTREE_ERR_INVALID_ARGUMENT
     assert c(P(FAKE), 48, 4, 4161, 96, 4096, 65, 16, P(FAKE), P(FAKE), None) == bd.DDTREE_ERR_UNSUPPORTED
     assert c(P(FAKE + 8), 48, 4, 4161, 128, 4096, 65, 16, P(FAKE), P(FAKE), None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+
+
+def test_target_argmax_validation(lib):
+    a = lib.ddtree_target_argmax
+    F32, BF16 = bd.DDTREE_DTYPE_F32, bd.DDTREE_DTYPE_BF16
+    WS = 65 * 32 * 8  # 32 chunks of the 152k-entry bf16 row
+    assert a(P(FAKE), F32, 151936, 0, 151936, P(FAKE), P(FAKE), WS, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert a(P(FAKE), F32, 151936, 65, 0, P(FAKE), P(FAKE), WS, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert a(P(FAKE), 7, 151936, 65, 151936, P(FAKE), P(FAKE), WS, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert a(P(FAKE), F32, 100, 65, 151936, P(FAKE), P(FAKE), WS, None) == bd.DDTREE_ERR_INVALID_ARGUMENT  # stride < V
+    assert a(P(FAKE + 2), F32, 151936, 65, 151936, P(FAKE), P(FAKE), WS, None) == bd.DDTREE_ERR_INVALID_ARGUMENT  # fp32 misaligned
+    assert a(None, BF16, 151936, 65, 151936, P(FAKE), P(FAKE), WS, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert a(P(FAKE), BF16, 151936, 65, 151936, None, P(FAKE), WS, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert a(P(FAKE), BF16, 151936, 65, 151936, P(FAKE), None, WS, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert a(P(FAKE), BF16, 151936, 65, 151936, P(FAKE), P(FAKE + 4), WS, None) == bd.DDTREE_ERR_INVALID_ARGUMENT  # ws misaligned
+    assert a(P(FAKE), BF16, 151936, 65, 151936, P(FAKE), P(FAKE), WS - 1, None) == bd.DDTREE_ERR_WORKSPACE_TOO_SMALL
+    assert a(P(FAKE), BF16, 151936, 1026, 151936, P(FAKE), P(FAKE), 1 << 20, None) == bd.DDTREE_ERR_UNSUPPORTED
+    assert a(P(FAKE), BF16, 1 << 23, 65, (1 << 22) + 1, P(FAKE), P(FAKE), WS, None) == bd.DDTREE_ERR_UNSUPPORTED
+    nb = ctypes.c_size_t(0)
+    assert lib.ddtree_target_argmax_workspace_bytes(BF16, 65, 151936, ctypes.byref(nb)) == 0
+    assert nb.value == WS
+    assert lib.ddtree_target_argmax_workspace_bytes(BF16, 0, 151936, ctypes.byref(nb)) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert lib.ddtree_target_argmax_workspace_bytes(BF16, 65, 151936, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
