@@ -19,10 +19,12 @@ tree          prefix scores, the order on prefixes, the top-B set
               (brute force, sort-and-expand, best-first heap), tree arrays
               and the ancestor-or-self mask
 attention     ancestor-only tree attention (naive, fp64)
-commit        greedy accept walk and KV-cache compaction
+commit        target argmax, greedy accept walk and KV-cache compaction
+sampling      temperature > 0: Philox4x32-10 uniforms, Gumbel-max target
+              sample per node (the walk then runs on the samples)
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against values the pages print, closed forms, theorems checked by
 exhaustive enumeration, or textbook/library reductions.
 """
-from . import attention, commit, softmax_topk, tree  # noqa: F401
+from . import attention, commit, sampling, softmax_topk, tree  # noqa: F401
