@@ -234,6 +234,7 @@ def main():
     stage["kv_compact"] = timed(lambda i=0: rnd.compact(kv, w.S), R)
     stage["target_argmax"] = timed(lambda i=0: rnd.target_argmax(tlog), R)
     argmax_ok = bool(torch.equal(rnd.target_choice, tgt))
+    stage["target_sample"] = timed(lambda i=0: rnd.target_sample(tlog, 1.0, 2024, i), R)
     if graph is None:
         attn_live = [a.elapsed_time(b) * 1e3 / w.layers for a, b in attn_pairs]
         attn_us = float(np.mean(attn_live))
@@ -284,6 +285,7 @@ def main():
         "topk_TBps": round(topk_bytes(w) / (stage["topk"] * 1e-6) / 1e12, 3),
         "target_argmax_TBps": round(argmax_bytes(w) / (stage["target_argmax"] * 1e-6) / 1e12, 3),
         "target_argmax_matches": argmax_ok,
+        "target_sample_Gtok_s": round(w.N * w.V / (stage["target_sample"] * 1e-6) / 1e9, 1),
         "accepted": a_acc,
         "depth_hist": np.bincount(depth).tolist(),
         "roofline": roof,

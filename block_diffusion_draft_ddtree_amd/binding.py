@@ -28,6 +28,7 @@ DDTREE_DTYPE_F32, DDTREE_DTYPE_BF16 = 0, 1
 _lib = None
 _vp, _i32, _i64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                               ctypes.c_float, ctypes.c_size_t)
+_u64 = ctypes.c_uint64
 
 _SIGNATURES = {
     "ddtree_status_string": (ctypes.c_char_p, [_i32]),
@@ -40,6 +41,8 @@ _SIGNATURES = {
                                 _i32, _vp, _vp, _sz, _vp]),
     "ddtree_target_argmax_workspace_bytes": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "ddtree_target_argmax": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "ddtree_target_sample": (_i32, [_vp, _i32, _i64, _i32, _i32, _f32, _u64, _u64, _vp, _vp, _sz,
+                                    _vp]),
     "ddtree_accept_walk": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "ddtree_kv_compact": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
 }
@@ -205,6 +208,28 @@ def ddtree_target_argmax(logits: torch.Tensor, out=None, ws=None, stream=None) -
                                       _dev(out, torch.int32, "out"), ws.data_ptr(), ws.numel(),
                                       _stream(stream)),
            "ddtree_target_argmax")
+    return out
+
+
+def ddtree_target_sample(logits: torch.Tensor, temperature: float, seed: int, offset: int,
+                         out=None, ws=None, stream=None) -> torch.Tensor:
+    """fp32 or bf16 logits [N, V] (row stride may exceed V) -> int32 [N]: one
+    token per node drawn from softmax(logits / temperature) (Gumbel-max over
+    Philox4x32-10 uniforms keyed by seed, counter offset)."""
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [N, V] with unit column stride")
+    if not logits.is_cuda or logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be a float32 or bfloat16 device tensor")
+    N, V = logits.shape
+    dtype = DDTREE_DTYPE_BF16 if logits.dtype == torch.bfloat16 else DDTREE_DTYPE_F32
+    if ws is None:
+        ws = workspace(ddtree_target_argmax_workspace_bytes(dtype, N, V), logits.device)
+    out = torch.empty(N, dtype=torch.int32, device=logits.device) if out is None else out
+    _check(lib().ddtree_target_sample(logits.data_ptr(), dtype, logits.stride(0), N, V,
+                                      float(temperature), int(seed) & (2**64 - 1),
+                                      int(offset) & (2**64 - 1), _dev(out, torch.int32, "out"),
+                                      ws.data_ptr(), ws.numel(), _stream(stream)),
+           "ddtree_target_sample")
     return out
 
 

@@ -149,6 +149,26 @@ DDT_API int ddtree_target_argmax(const void* logits, int dtype, int64_t row_stri
                                  stream);
 }
 
+DDT_API int ddtree_target_sample(const void* logits, int dtype, int64_t row_stride, int N, int V,
+                                 float temperature, uint64_t seed, uint64_t offset, int32_t* out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int st = argmax_check(dtype, N, V);
+  if (st) return st;
+  if (!logits || !out || !ws) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (row_stride < V) return DDTREE_ERR_INVALID_ARGUMENT;
+  const uintptr_t esize = dtype == DDTREE_DTYPE_BF16 ? 2u : 4u;
+  if (reinterpret_cast<uintptr_t>(logits) % esize != 0) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(ws) % 8 != 0) return DDTREE_ERR_INVALID_ARGUMENT;
+  // T > 0 and log2(e) / T a finite, normal fp32 number.
+  if (!(temperature > 0.f) || !(temperature <= 3.0e38f)) return DDTREE_ERR_INVALID_ARGUMENT;
+  const double c = 1.4426950408889634 / (double)temperature;
+  if (!(c <= 3.0e38) || c < 1.2e-38) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < ddt_host::argmax_workspace_bytes(N, V, (int)esize))
+    return DDTREE_ERR_WORKSPACE_TOO_SMALL;
+  return ddt_host::sample_launch(logits, dtype == DDTREE_DTYPE_BF16, row_stride, N, V, (float)c,
+                                 seed, offset, ws, out, stream);
+}
+
 DDT_API int ddtree_accept_walk(const int32_t* parent, const int32_t* node_token, int N, int L,
                                const int32_t* target_argmax, int32_t* acc, int32_t* n_acc,
                                int32_t* next_bonus, hipStream_t stream) {

@@ -37,6 +37,8 @@ int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int S, 
 size_t argmax_workspace_bytes(int N, int V, int dtype_bytes);
 int argmax_launch(const void* logits, int bf16, int64_t row_stride, int N, int V, void* ws,
                   int32_t* out, hipStream_t stream);
+int sample_launch(const void* logits, int bf16, int64_t row_stride, int N, int V, float log2e_over_t,
+                  uint64_t seed, uint64_t offset, void* ws, int32_t* out, hipStream_t stream);
 
 int walk_launch(const int32_t* parent, const int32_t* tok, int N, int L, const int32_t* tgt,
                 int32_t* acc, int32_t* n_acc, int32_t* bonus, hipStream_t stream);

@@ -1,5 +1,6 @@
 """One DDTree decode round on the device: topk -> build -> tree attention per
-layer -> (target argmax) -> accept walk -> KV compaction ("DDTree Deep
+layer -> (target argmax, or target sample at temperature > 0) -> accept walk
+-> KV compaction ("DDTree Deep
 Dive", section 3: the draft, tree_build, tree_compile, verify, commit
 stages; the drafter forward and the target's non-attention layers, LM head
 included, are outside this library).
@@ -76,6 +77,12 @@ class DraftTreeRound:
     def target_argmax(self, target_logits):
         """bf16 [N, V] target head logits -> the target's greedy token per node."""
         return bd.ddtree_target_argmax(target_logits, out=self.target_choice, ws=self.ws_argmax)
+
+    def target_sample(self, target_logits, temperature: float, seed: int, offset: int):
+        """Temperature > 0: the target's sampled token per node (the walk then
+        runs on these); pass a fresh offset every round."""
+        return bd.ddtree_target_sample(target_logits, temperature, seed, offset,
+                                       out=self.target_choice, ws=self.ws_argmax)
 
     def walk(self, target_argmax):
         bd.ddtree_accept_walk(self.parent, self.node_token, self.shape.L, target_argmax,

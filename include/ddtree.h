@@ -7,6 +7,7 @@
  *   ddtree_build        best-first top-B prefix tree, node arrays, ancestor mask
  *   ddtree_tree_attn    ancestor-only GQA attention of the tree nodes (per layer)
  *   ddtree_target_argmax  the target's greedy token after every tree node
+ *   ddtree_target_sample  the target's sampled token (temperature > 0)
  *   ddtree_accept_walk  greedy walk of the target's argmax down the tree
  *   ddtree_kv_compact   in-place gather of the accepted path's K/V rows
  *
@@ -191,6 +192,44 @@ int ddtree_tree_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 int ddtree_target_argmax_workspace_bytes(int dtype, int N, int V, size_t* bytes /* host */);
 int ddtree_target_argmax(const void* logits, int dtype, int64_t row_stride, int N, int V,
                          int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * ddtree_target_sample -- the target's token per tree node at temperature > 0.
+ *
+ * Source: [DD] section 6 (the target samples its token at each node, the
+ * walk descends into the child holding it, the first token with no such
+ * child is the bonus; at temperature > 0 the usual speculative-sampling
+ * rules keep the output distributed as the target's). The children of a
+ * node are fixed drafts, for which that rule reduces to: draw the token from
+ * the target and follow it, so ddtree_accept_walk run on these samples is
+ * the temperature > 0 verification.
+ *
+ * Draws out[n] from softmax(logits[n] / temperature) by the Gumbel-max rule,
+ * out[n] = argmax_v (logits[n][v] / T - ln(-ln u[n][v])), with the uniforms
+ * from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011):
+ *   key     = (seed mod 2^32, seed >> 32)
+ *   counter = (v >> 2, n, offset mod 2^32, offset >> 32), output word v & 3
+ *   u       = ((word >> 9) + 0.5) * 2^-23   (exact in fp32, inside (0, 1))
+ * so a result is a pure function of (logits, T, seed, offset): pass a new
+ * offset every round. The key is formed in fp32 (in base 2, the same
+ * argmax); it can pick differently from an exact evaluation only where two
+ * tokens' keys are within fp32 rounding of each other.
+ *
+ * logits, dtype, row_stride, N, V  as for ddtree_target_argmax; -inf marks
+ *             a token that is never drawn; each row needs a finite logit.
+ *             |logit| * log2(e) / T must stay below 3e38.
+ * temperature T > 0, with log2(e) / T a normal fp32 number.
+ * seed, offset  the draw's Philox key and counter words (see above).
+ * out         out int32 [N]: the sampled token per node; the target_argmax
+ *             argument of ddtree_accept_walk.
+ * ws/ws_bytes as for ddtree_target_argmax (same size query).
+ *
+ * One streaming pass over N * V elements plus one Philox block per four
+ * tokens; ALU-bound at the 30B shape.
+ * ---------------------------------------------------------------------- */
+int ddtree_target_sample(const void* logits, int dtype, int64_t row_stride, int N, int V,
+                         float temperature, uint64_t seed, uint64_t offset, int32_t* out,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * ddtree_accept_walk -- greedy verification walk down the tree.

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(bd.EXPORTS)
@@ -132,3 +132,26 @@ def test_target_argmax_validation(lib):
     assert nb.value == WS
     assert lib.ddtree_target_argmax_workspace_bytes(BF16, 0, 151936, ctypes.byref(nb)) == bd.DDTREE_ERR_INVALID_ARGUMENT
     assert lib.ddtree_target_argmax_workspace_bytes(BF16, 65, 151936, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+
+
+def test_target_sample_validation(lib):
+    f = lib.ddtree_target_sample
+    BF16 = bd.DDTREE_DTYPE_BF16
+    WS = 65 * 32 * 8
+
+    def call(logits=P(FAKE), dtype=BF16, stride=151936, N=65, V=151936, T=1.0, out=P(FAKE),
+             w=P(FAKE), ws=WS):
+        return f(logits, dtype, stride, N, V, T, 1, 2, out, w, ws, None)
+
+    for T in (0.0, -1.0, float("nan"), float("inf"), 1e-39):
+        assert call(T=T) == bd.DDTREE_ERR_INVALID_ARGUMENT, T
+    assert call(T=3e38) == bd.DDTREE_ERR_INVALID_ARGUMENT  # log2(e) / T below fp32 normals
+    assert call(N=0) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert call(dtype=5) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert call(stride=10) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert call(logits=None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert call(out=None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert call(w=None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert call(w=P(FAKE + 4)) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert call(ws=WS - 1) == bd.DDTREE_ERR_WORKSPACE_TOO_SMALL
+    assert call(N=1026, ws=1 << 20) == bd.DDTREE_ERR_UNSUPPORTED
