@@ -20,6 +20,8 @@ tree          prefix scores, the order on prefixes, the top-B set
               and the ancestor-or-self mask
 attention     ancestor-only tree attention (naive, fp64)
 commit        target argmax, greedy accept walk and KV-cache compaction
+budget        cost-aware node budget from the pop-order scores
+              (Proposition 1's expected acceptance per budget)
 sampling      temperature > 0: Philox4x32-10 uniforms, Gumbel-max target
               sample per node (the walk then runs on the samples)
 
@@ -27,4 +29,4 @@ Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against values the pages print, closed forms, theorems checked by
 exhaustive enumeration, or textbook/library reductions.
 """
-from . import attention, commit, sampling, softmax_topk, tree  # noqa: F401
+from . import attention, budget, commit, sampling, softmax_topk, tree  # noqa: F401
