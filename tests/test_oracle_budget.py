@@ -35,12 +35,12 @@ def test_limits_of_the_cost_model():
     assert ob.select_budget(score, 1.0, 0.0) == 5
     # Verification dominated by per-node cost: 1 / (B + 1) shape, smallest B.
     assert ob.select_budget(score, 0.0, 1.0, B_min=1) == 1
-    # Equal objectives pick the smaller budget: with t0 = t1 = 1,
-    # (1 + 0.5) / 3 == (1 + 1.0) / 4.
-    tie = np.log(np.array([1.0, 0.5, 0.5]))
-    obj = ob.budget_objective(tie, 1.0, 1.0)
-    assert obj[1] == obj[2]
-    assert ob.select_budget(tie, 1.0, 1.0, B_min=1) == 1
+    # Equal objectives pick the smaller budget: two certain pops (q = 1)
+    # with t0 = 0 give 2 / 2 == 3 / 3 exactly.
+    tie = np.zeros(3, dtype=np.float32)
+    obj = ob.budget_objective(tie, 0.0, 1.0)
+    assert obj[1] == obj[2] == 1.0
+    assert ob.select_budget(tie, 0.0, 1.0, B_min=1) == 1
 
 
 @pytest.mark.parametrize("seed", range(3))
