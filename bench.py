@@ -33,6 +33,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 ATTN_SOURCE = os.path.join(ROOT, "block_diffusion_draft_ddtree_amd", "csrc", "attn.hip")
 COPY_PROBE_BYTES = 256 << 20  # bytes read and bytes written by the copy probe
 SPIN_CYCLES = 10_000_000      # ~5 ms of device spin ahead of each stage's timed reps
+# Round time t0 + t1 * nodes fitted to the autobench Qwen3-Coder-30B page's
+# budget-64 and budget-256 rows (tokens per step / tokens per second).
+BUDGET_T1 = (3.69 / 17.32 - 3.22 / 20.75) / (257 - 65)
+BUDGET_T0 = 3.22 / 20.75 - BUDGET_T1 * 65
 
 
 def traffic_summary_path(workload: str) -> str:
@@ -235,6 +239,8 @@ def main():
     stage["target_argmax"] = timed(lambda i=0: rnd.target_argmax(tlog), R)
     argmax_ok = bool(torch.equal(rnd.target_choice, tgt))
     stage["target_sample"] = timed(lambda i=0: rnd.target_sample(tlog, 1.0, 2024, i), R)
+    stage["budget_select"] = timed(lambda i=0: rnd.select_budget(BUDGET_T0, BUDGET_T1), R)
+    budget_choice = int(rnd.budget.cpu()[0])
     if graph is None:
         attn_live = [a.elapsed_time(b) * 1e3 / w.layers for a, b in attn_pairs]
         attn_us = float(np.mean(attn_live))
@@ -286,6 +292,7 @@ def main():
         "target_argmax_TBps": round(argmax_bytes(w) / (stage["target_argmax"] * 1e-6) / 1e12, 3),
         "target_argmax_matches": argmax_ok,
         "target_sample_Gtok_s": round(w.N * w.V / (stage["target_sample"] * 1e-6) / 1e9, 1),
+        "budget_choice": budget_choice,
         "accepted": a_acc,
         "depth_hist": np.bincount(depth).tolist(),
         "roofline": roof,

@@ -41,6 +41,8 @@ _SIGNATURES = {
                                 _i32, _vp, _vp, _sz, _vp]),
     "ddtree_target_argmax_workspace_bytes": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "ddtree_target_argmax": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "ddtree_budget_select": (_i32, [_vp, _i32, _i32, ctypes.c_double, ctypes.c_double, _vp, _vp,
+                                    _vp]),
     "ddtree_target_sample": (_i32, [_vp, _i32, _i64, _i32, _i32, _f32, _u64, _u64, _vp, _vp, _sz,
                                     _vp]),
     "ddtree_accept_walk": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
@@ -231,6 +233,22 @@ def ddtree_target_sample(logits: torch.Tensor, temperature: float, seed: int, of
                                       ws.data_ptr(), ws.numel(), _stream(stream)),
            "ddtree_target_sample")
     return out
+
+
+def ddtree_budget_select(score: torch.Tensor, B_max: int, t0: float, t1: float, B_min: int = 1,
+                         expected=None, budget=None, stream=None):
+    """fp32 scores [>= B_max + 1] from ddtree_build -> (budget int32 [1],
+    expected fp32 [B_max + 1]) on the device."""
+    dev = score.device
+    expected = torch.empty(B_max + 1, dtype=torch.float32, device=dev) if expected is None else expected
+    budget = torch.empty(1, dtype=torch.int32, device=dev) if budget is None else budget
+    if score.numel() < B_max + 1 or expected.numel() < B_max + 1:
+        raise ValueError("score and expected need B_max + 1 entries")
+    _check(lib().ddtree_budget_select(_dev(score, torch.float32, "score"), B_max, B_min, float(t0),
+                                      float(t1), _dev(expected, torch.float32, "expected"),
+                                      _dev(budget, torch.int32, "budget"), _stream(stream)),
+           "ddtree_budget_select")
+    return budget, expected
 
 
 def ddtree_accept_walk(parent: torch.Tensor, node_token: torch.Tensor, L: int,

@@ -169,6 +169,16 @@ DDT_API int ddtree_target_sample(const void* logits, int dtype, int64_t row_stri
                                  seed, offset, ws, out, stream);
 }
 
+DDT_API int ddtree_budget_select(const float* score, int B_max, int B_min, double t0, double t1,
+                                 float* expected, int32_t* budget, hipStream_t stream) {
+  if (B_max < 1 || B_min < 0 || B_min > B_max) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (B_max > DDTREE_MAX_B) return DDTREE_ERR_UNSUPPORTED;
+  if (!score || !budget) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (!(t0 >= 0.0) || !(t1 >= 0.0) || !(t0 <= 1e300) || !(t1 <= 1e300) || !(t0 + t1 > 0.0))
+    return DDTREE_ERR_INVALID_ARGUMENT;
+  return ddt_host::budget_launch(score, B_max, B_min, t0, t1, expected, budget, stream);
+}
+
 DDT_API int ddtree_accept_walk(const int32_t* parent, const int32_t* node_token, int N, int L,
                                const int32_t* target_argmax, int32_t* acc, int32_t* n_acc,
                                int32_t* next_bonus, hipStream_t stream) {

@@ -40,6 +40,9 @@ int argmax_launch(const void* logits, int bf16, int64_t row_stride, int N, int V
 int sample_launch(const void* logits, int bf16, int64_t row_stride, int N, int V, float log2e_over_t,
                   uint64_t seed, uint64_t offset, void* ws, int32_t* out, hipStream_t stream);
 
+int budget_launch(const float* score, int B_max, int B_min, double t0, double t1,
+                  float* expected, int32_t* budget, hipStream_t stream);
+
 int walk_launch(const int32_t* parent, const int32_t* tok, int N, int L, const int32_t* tgt,
                 int32_t* acc, int32_t* n_acc, int32_t* bonus, hipStream_t stream);
 int compact_launch(uint16_t* kv, int layers, int Hkv, int S_cap, int D, int S,

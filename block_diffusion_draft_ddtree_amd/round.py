@@ -59,6 +59,8 @@ class DraftTreeRound:
         self.target_choice = torch.empty(s.N, **i32)
         self.ws_argmax = bd.workspace(
             bd.ddtree_target_argmax_workspace_bytes(bd.DDTREE_DTYPE_BF16, s.N, s.V), dev)
+        self.budget = torch.empty(1, **i32)
+        self.expected_accept = torch.empty(s.N, dtype=torch.float32, device=dev)
         self.acc = torch.empty(s.L + 1, **i32)
         self.n_acc = torch.empty(1, **i32)
         self.next_bonus = torch.empty(1, **i32)
@@ -73,6 +75,12 @@ class DraftTreeRound:
     def attn(self, layer: int, q, kv, S: int):
         bd.ddtree_tree_attn(q[layer], kv[layer, 0], kv[layer, 1], S, self.anc,
                             out=self.attn_out[layer], ws=self.ws_attn)
+
+    def select_budget(self, t0: float, t1: float, B_min: int = 1):
+        """Cost-aware budget over this round's tree: the first budget[0] + 1
+        nodes form the tree to verify (round time model t0 + t1 * nodes)."""
+        return bd.ddtree_budget_select(self.score, self.shape.B, t0, t1, B_min,
+                                       expected=self.expected_accept, budget=self.budget)
 
     def target_argmax(self, target_logits):
         """bf16 [N, V] target head logits -> the target's greedy token per node."""

@@ -8,6 +8,7 @@
  *   ddtree_tree_attn    ancestor-only GQA attention of the tree nodes (per layer)
  *   ddtree_target_argmax  the target's greedy token after every tree node
  *   ddtree_target_sample  the target's sampled token (temperature > 0)
+ *   ddtree_budget_select  cost-aware node budget from the build's scores
  *   ddtree_accept_walk  greedy walk of the target's argmax down the tree
  *   ddtree_kv_compact   in-place gather of the accepted path's K/V rows
  *
@@ -230,6 +231,30 @@ int ddtree_target_argmax(const void* logits, int dtype, int64_t row_stride, int 
 int ddtree_target_sample(const void* logits, int dtype, int64_t row_stride, int N, int V,
                          float temperature, uint64_t seed, uint64_t offset, int32_t* out,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * ddtree_budget_select -- the node budget with the most expected tokens per
+ * unit of round time.
+ *
+ * Source: [DD] section 2, Proposition 1 (the expected accepted length of a
+ * tree under the drafter's distribution is the sum of q(u) = exp(score(u))
+ * over its nodes) and Propositions 2-3 (best-first pops are the top-B
+ * prefixes, so the budget-B tree is the first B + 1 nodes of one build with
+ * the largest budget, and its mask rows are unchanged); [AB] results and
+ * notes (the budget has an optimum where verification cost outgrows the
+ * acceptance gain; a cost-aware variant picks it).
+ *
+ * score     fp32 [B_max + 1] from ddtree_build (pop order, root first).
+ * B_max     1 <= B_max <= DDTREE_MAX_B; B_min: 0 <= B_min <= B_max.
+ * t0, t1    round time model t0 + t1 * (B + 1) (any unit), both finite,
+ *           >= 0, not both 0.
+ * expected  out fp32 [B_max + 1] or NULL: expected[B] = E[alpha] of the
+ *           budget-B tree = sum_{n=1..B} exp(score[n]) (summed in fp64).
+ * budget    out int32 [1]: the smallest B in [B_min, B_max] maximising
+ *           (1 + expected[B]) / (t0 + t1 * (B + 1)) (fp64).
+ * ---------------------------------------------------------------------- */
+int ddtree_budget_select(const float* score, int B_max, int B_min, double t0, double t1,
+                         float* expected, int32_t* budget, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * ddtree_accept_walk -- greedy verification walk down the tree.

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(bd.EXPORTS)
@@ -155,3 +155,17 @@ def test_target_sample_validation(lib):
     assert call(w=P(FAKE + 4)) == bd.DDTREE_ERR_INVALID_ARGUMENT
     assert call(ws=WS - 1) == bd.DDTREE_ERR_WORKSPACE_TOO_SMALL
     assert call(N=1026, ws=1 << 20) == bd.DDTREE_ERR_UNSUPPORTED
+
+
+def test_budget_select_validation(lib):
+    f = lib.ddtree_budget_select
+    E = bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert f(P(FAKE), 0, 0, 1.0, 0.1, None, P(FAKE), None) == E
+    assert f(P(FAKE), 64, 65, 1.0, 0.1, None, P(FAKE), None) == E
+    assert f(P(FAKE), 64, -1, 1.0, 0.1, None, P(FAKE), None) == E
+    assert f(P(FAKE), 1025, 1, 1.0, 0.1, None, P(FAKE), None) == bd.DDTREE_ERR_UNSUPPORTED
+    assert f(None, 64, 1, 1.0, 0.1, None, P(FAKE), None) == E
+    assert f(P(FAKE), 64, 1, 1.0, 0.1, None, None, None) == E
+    for t0, t1 in ((0.0, 0.0), (-1.0, 0.1), (1.0, -0.1), (float("nan"), 0.1), (float("inf"), 0.1),
+                   (1.0, float("inf"))):
+        assert f(P(FAKE), 64, 1, t0, t1, None, P(FAKE), None) == E, (t0, t1)

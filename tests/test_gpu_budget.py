@@ -1,0 +1,106 @@
+"""GPU parity: ddtree_budget_select against the oracle's cost-aware budget.
+
+Expected acceptance per budget is Proposition 1 of the "DDTree Deep Dive"
+page (section 2) over the first B pops; the budget maximises expected tokens
+per unit of round time (the autobench Qwen3-Coder-30B page's budget
+optimum). Both sides sum in fp64, in different orders, so the budget is
+compared exactly unless the oracle's best objective and the objective of the
+device's pick differ by less than 1e-12 relative, where either is right."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_draft_ddtree_amd import binding as bd
+from block_diffusion_draft_ddtree_amd import synth
+from oracle import budget as ob
+
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+# Round-time model fitted to the autobench page's two DDTree rows (budget 64:
+# 3.22 tokens per step at 20.75 tok/s; budget 256: 3.69 at 17.32 tok/s), in
+# seconds: t(B) = t0 + t1 (B + 1).
+_T1 = (3.69 / 17.32 - 3.22 / 20.75) / (257 - 65)
+_T0 = 3.22 / 20.75 - _T1 * 65
+
+
+def _table(g, B_max):
+    return np.concatenate([[0.0], -np.sort(g.exponential(1.5, size=B_max))]).astype(np.float32)
+
+
+def _check(score, B_max, B_min, t0, t1):
+    say(f"budget B_max={B_max} B_min={B_min} t0={t0:.4g} t1={t1:.4g}")
+    b, e = bd.ddtree_budget_select(torch.from_numpy(score).cuda(), B_max, t0, t1, B_min)
+    got_b, got_e = int(b.cpu()[0]), e.cpu().numpy()
+    want_e = ob.expected_accept(score[: B_max + 1])
+    np.testing.assert_allclose(got_e, want_e, rtol=2e-7, atol=1e-30)
+    obj = ob.budget_objective(score[: B_max + 1], t0, t1)
+    want_b = ob.select_budget(score[: B_max + 1], t0, t1, B_min, B_max)
+    if got_b != want_b:
+        assert B_min <= got_b <= B_max
+        assert obj[got_b] >= obj[want_b] * (1 - 1e-12), (got_b, want_b)
+    return got_b
+
+
+@pytest.mark.parametrize("B_max", [1, 2, 63, 64, 65, 257, 1000, 1024])
+def test_random_tables(B_max):
+    g = synth.rng("test", 690, B_max)
+    for _ in range(6):
+        score = _table(g, B_max)
+        t0 = float(g.uniform(0.0, 2.0))
+        t1 = float(10 ** g.uniform(-4, -0.5))
+        B_min = int(g.integers(0, B_max + 1)) if g.uniform() < 0.3 else 1
+        _check(score, B_max, B_min, t0, t1)
+
+
+def test_cost_model_from_the_pages_numbers():
+    g = synth.rng("test", 691, 0)
+    score = _table(g, 1024)
+    b = _check(score, 1024, 1, _T0, _T1)
+    assert 1 <= b <= 1024
+
+
+def test_exact_tie_picks_the_smaller_budget():
+    score = np.zeros(9, dtype=np.float32)  # eight certain pops
+    assert _check(score, 8, 1, 0.0, 1.0) == 1
+    assert _check(score, 8, 3, 0.0, 1.0) == 3
+
+
+def test_extremes_and_no_expected_output():
+    g = synth.rng("test", 692, 0)
+    score = _table(g, 300)
+    assert _check(score, 300, 1, 1.0, 0.0) == 300  # free verification
+    say("budget without expected output")
+    b = torch.empty(1, dtype=torch.int32, device="cuda")
+    lib = bd.lib()
+    st = lib.ddtree_budget_select(torch.from_numpy(score).cuda().data_ptr(), 300, 1, 1.0, 0.05,
+                                  None, b.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    assert int(b.cpu()[0]) == ob.select_budget(score, 1.0, 0.05, 1, 300)
+
+
+def test_on_device_build_scores():
+    """ddtree_topk -> ddtree_build (budget 256) -> ddtree_budget_select on
+    the device, against the oracle on the downloaded scores."""
+    w = synth.WORKLOADS["coder30b_b64_deep"]
+    lg = synth.drafter_logits(w, 0)
+    L, K, B_max = w.L, 64, 256
+    say("budget on device build scores")
+    logits = torch.from_numpy(lg.x).cuda()
+    logp = torch.empty((L, K), dtype=torch.float32, device="cuda")
+    token = torch.empty((L, K), dtype=torch.int32, device="cuda")
+    ws = bd.workspace(bd.ddtree_topk_workspace_bytes(L, w.V, K), "cuda")
+    bd.ddtree_topk(logits, K, logp, token, ws)
+    N = B_max + 1
+    W = (N + 31) // 32
+    i32 = dict(dtype=torch.int32, device="cuda")
+    root = torch.zeros(1, **i32)
+    parent, depth, tok = torch.empty(N, **i32), torch.empty(N, **i32), torch.empty(N, **i32)
+    score = torch.empty(N, dtype=torch.float32, device="cuda")
+    anc = torch.empty((N, W), **i32)
+    bd.ddtree_build(logp, token, B_max, root, W, parent, depth, tok, score, anc)
+    b, e = bd.ddtree_budget_select(score, B_max, _T0, _T1, 1)
+    s_np = score.cpu().numpy()
+    np.testing.assert_allclose(e.cpu().numpy(), ob.expected_accept(s_np), rtol=2e-7, atol=1e-30)
+    assert int(b.cpu()[0]) == ob.select_budget(s_np, _T0, _T1, 1, B_max)
