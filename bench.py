@@ -89,6 +89,8 @@ def parse():
     ap.add_argument("--stage-reps", type=int, default=30)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only the plain copy used to scale the byte counters")
+    ap.add_argument("--batch-requests", type=int, default=8,
+                    help="requests in the batched-round leg (0 skips it)")
     return ap.parse_args()
 
 
@@ -298,9 +300,79 @@ def main():
         "roofline": roof,
     }
 
+    if args.batch_requests > 0:
+        result["batched"] = batched_leg(w, args.batch_requests, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, lg, depth, tgt_np)
     print(json.dumps(result), flush=True)
+
+
+# Prefix lengths of the batched leg: R requests of the same model shape with
+# contexts from 512 to 4096 tokens, taken in this order.
+BATCH_S = [4096, 1024, 3072, 2048, 4096, 512, 3584, 2560]
+
+
+def batched_leg(w, R: int, steps: int, warmup: int):
+    """R requests of workload w in one batched round (own drafter rows,
+    tree, prefix length and KV cache each): topk over the stacked rows,
+    build, every layer's attention, walk, compaction. Inputs are drawn on
+    the device from a seeded generator."""
+    import torch
+
+    from block_diffusion_draft_ddtree_amd.round import BatchedDraftTreeRound, RoundShape
+
+    dev = torch.device("cuda:0")
+    S = [BATCH_S[r % len(BATCH_S)] for r in range(R)]
+    S_cap = max(S) + w.N
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20240 + R)
+    logits = 2.0 * torch.randn((R * w.L, w.V), generator=gen, device=dev)
+    q = torch.randn((w.layers, R, w.N, w.Hq, w.D), generator=gen, device=dev).to(torch.bfloat16)
+    kv = torch.empty((R, w.layers, 2, w.Hkv, S_cap, w.D), dtype=torch.bfloat16, device=dev)
+    for r in range(R):
+        kv[r].copy_(torch.randn(kv[r].shape, generator=gen, device=dev))
+    target = torch.randint(0, w.V, (R, w.N), generator=gen, device=dev, dtype=torch.int32)
+    shape = RoundShape(w.L, w.V, w.K, w.B, w.Hq, w.Hkv, w.D, w.layers, S_cap)
+    rnd = BatchedDraftTreeRound(shape, S, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(attn_ev=None):
+        rnd.topk(logits)
+        rnd.build()
+        if attn_ev is not None:
+            attn_ev[0].record(stream)
+        for layer in range(w.layers):
+            rnd.attn(layer, q[layer], kv)
+        if attn_ev is not None:
+            attn_ev[1].record(stream)
+        rnd.walk(target)
+        rnd.compact(kv)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    pairs = [(ev(), ev()) for _ in range(steps)]
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for i in range(steps):
+        step(pairs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    round_us = e0.elapsed_time(e1) * 1e3 / steps
+    attn_us = float(np.mean([a.elapsed_time(b) * 1e3 / w.layers for a, b in pairs]))
+    # Algorithmic bytes of one batched attention launch: every request's
+    # prefix and tree K/V, Q in, O out, the mask rows.
+    W = (w.N + 31) // 32
+    nbytes = sum(4 * w.Hkv * (s + w.N) * w.D + 4 * w.N * w.Hq * w.D + 4 * w.N * W for s in S)
+    depth = rnd.tree[1].cpu().numpy()
+    flops = sum(4 * w.N * w.Hq * w.D * s for s in S) + 4 * w.Hq * w.D * int((depth + 1).sum())
+    return {"R": R, "S": S, "round_us": round(round_us, 2),
+            "us_per_request": round(round_us / R, 2),
+            "tree_attn_us": round(attn_us, 3),
+            "tree_attn_TBps": round(nbytes / (attn_us * 1e-6) / 1e12, 3),
+            "tree_attn_TFLOPs": round(flops / (attn_us * 1e-6) / 1e12, 1),
+            "data": "synthetic (seeded torch device generator)"}
 
 
 def cpu_baseline(w, lg, depth, tgt_np):

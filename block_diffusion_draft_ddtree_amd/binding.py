@@ -47,6 +47,15 @@ _SIGNATURES = {
                                     _vp]),
     "ddtree_accept_walk": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "ddtree_kv_compact": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "ddtree_build_batched": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _i32, _vp]),
+    "ddtree_tree_attn_batched_workspace_bytes": (_i32, [_i32, _vp, _i32, _i32, _i32, _i32,
+                                                        ctypes.POINTER(_sz)]),
+    "ddtree_tree_attn_batched": (_i32, [_vp, _vp, _vp, _i64, _i32, _vp, _i32, _i32, _i32, _i32,
+                                        _i32, _f32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "ddtree_accept_walk_batched": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "ddtree_kv_compact_batched": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _i32, _vp,
+                                         _vp, _vp]),
 }
 EXPORTS = tuple(_SIGNATURES)
 
@@ -279,3 +288,94 @@ def ddtree_kv_compact(kv: torch.Tensor, S: int, N: int, L: int, acc: torch.Tenso
         _dev(kv, torch.bfloat16, "kv"), layers, Hkv, S_cap, D, S, N, L,
         _dev(acc, torch.int32, "acc"), _dev(n_acc, torch.int32, "n_acc"), _stream(stream)),
         "ddtree_kv_compact")
+
+
+# ---- several requests per call ---------------------------------------------
+
+def _host_ints(values) -> ctypes.Array:
+    vals = [int(x) for x in values]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def ddtree_build_batched(logp: torch.Tensor, token: torch.Tensor, B: int,
+                         root_token: torch.Tensor, mask_words: int | None = None, stream=None):
+    """[R, L, K] tables, root_token int32 [R] -> (parent, depth, node_token,
+    score) int32/fp32 [R, B + 1] and anc [R, B + 1, W]."""
+    R, L, K = logp.shape
+    N = B + 1
+    W = (N + 31) // 32 if mask_words is None else mask_words
+    dev = logp.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    parent, depth, node_token = (torch.empty((R, N), **i32) for _ in range(3))
+    score = torch.empty((R, N), dtype=torch.float32, device=dev)
+    anc = torch.empty((R, N, W), **i32)
+    _check(lib().ddtree_build_batched(
+        _dev(logp, torch.float32, "logp"), _dev(token, torch.int32, "token"), L, K, B, R,
+        _dev(root_token, torch.int32, "root_token"), _dev(parent, torch.int32, "parent"),
+        _dev(depth, torch.int32, "depth"), _dev(node_token, torch.int32, "node_token"),
+        _dev(score, torch.float32, "score"), _dev(anc, torch.int32, "anc"), W, _stream(stream)),
+        "ddtree_build_batched")
+    return parent, depth, node_token, score, anc
+
+
+def ddtree_tree_attn_batched_workspace_bytes(S, N: int, Hq: int, Hkv: int, D: int) -> int:
+    out = _sz(0)
+    _check(lib().ddtree_tree_attn_batched_workspace_bytes(len(S), _host_ints(S), N, Hq, Hkv, D,
+                                                          ctypes.byref(out)),
+           "ddtree_tree_attn_batched_workspace_bytes")
+    return out.value
+
+
+def ddtree_tree_attn_batched(q: torch.Tensor, kv: torch.Tensor, layer: int, S, anc: torch.Tensor,
+                             scale: float | None = None, out=None, ws=None, stream=None):
+    """q bf16 [R, N, Hq, D]; kv bf16 [R, layers, 2, Hkv, S_cap, D] (layer's
+    K and V of every request); S host ints [R]; anc [R, N, W] -> out bf16
+    [R, N, Hq, D]."""
+    R, N, Hq, D = q.shape
+    R2, layers, two, Hkv, S_cap, Dk = kv.shape
+    if R2 != R or two != 2 or Dk != D or len(S) != R:
+        raise ValueError("kv must be [R, layers, 2, Hkv, S_cap, D] matching q, S one per request")
+    if not kv.is_contiguous() or kv.dtype != torch.bfloat16 or not kv.is_cuda:
+        raise ValueError("kv must be a contiguous bf16 device tensor")
+    if anc.dim() != 3 or anc.shape[0] != R or anc.shape[1] < N:
+        raise ValueError("anc must be [R, N, mask_words]")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    if ws is None:
+        ws = workspace(ddtree_tree_attn_batched_workspace_bytes(S, N, Hq, Hkv, D), q.device)
+    stride = layers * 2 * Hkv * S_cap * D
+    _check(lib().ddtree_tree_attn_batched(
+        _dev(q, torch.bfloat16, "q"), kv[0, layer, 0].data_ptr(), kv[0, layer, 1].data_ptr(),
+        stride, R, _host_ints(S), S_cap, N, Hq, Hkv, D, scale, _dev(anc, anc.dtype, "anc"),
+        anc.shape[2], _dev(out, torch.bfloat16, "out"), _dev(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream)), "ddtree_tree_attn_batched")
+    return out
+
+
+def ddtree_accept_walk_batched(parent: torch.Tensor, node_token: torch.Tensor, L: int,
+                               target: torch.Tensor, stream=None):
+    """[R, N] trees and target tokens -> (acc int32 [R, L + 1], n_acc int32
+    [R], next_bonus int32 [R])."""
+    R, N = parent.shape
+    i32 = dict(dtype=torch.int32, device=parent.device)
+    acc = torch.empty((R, L + 1), **i32)
+    n_acc = torch.empty(R, **i32)
+    next_bonus = torch.empty(R, **i32)
+    _check(lib().ddtree_accept_walk_batched(
+        _dev(parent, torch.int32, "parent"), _dev(node_token, torch.int32, "node_token"), N, L, R,
+        _dev(target, torch.int32, "target"), _dev(acc, torch.int32, "acc"),
+        _dev(n_acc, torch.int32, "n_acc"), _dev(next_bonus, torch.int32, "next_bonus"),
+        _stream(stream)), "ddtree_accept_walk_batched")
+    return acc, n_acc, next_bonus
+
+
+def ddtree_kv_compact_batched(kv: torch.Tensor, S, N: int, L: int, acc: torch.Tensor,
+                              n_acc: torch.Tensor, stream=None) -> None:
+    """In place on kv bf16 [R, layers, 2, Hkv, S_cap, D]; S host ints [R]."""
+    R, layers, two, Hkv, S_cap, D = kv.shape
+    if two != 2 or len(S) != R:
+        raise ValueError("kv must be [R, layers, 2, Hkv, S_cap, D], S one per request")
+    _check(lib().ddtree_kv_compact_batched(
+        _dev(kv, torch.bfloat16, "kv"), layers, Hkv, S_cap, D, R, _host_ints(S), N, L,
+        _dev(acc, torch.int32, "acc"), _dev(n_acc, torch.int32, "n_acc"), _stream(stream)),
+        "ddtree_kv_compact_batched")

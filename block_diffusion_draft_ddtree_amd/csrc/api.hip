@@ -30,7 +30,7 @@ bool enough_prefixes(int L, int K, int B) {
 int topk_check(int L, int V, int K) {
   if (L < 1 || V < 1 || K < 1) return DDTREE_ERR_INVALID_ARGUMENT;
   if (K > V) return DDTREE_ERR_INVALID_ARGUMENT;
-  if (L > DDTREE_MAX_L || K > DDTREE_MAX_K) return DDTREE_ERR_UNSUPPORTED;
+  if (L > DDTREE_MAX_L * DDTREE_MAX_REQ || K > DDTREE_MAX_K) return DDTREE_ERR_UNSUPPORTED;
   if (V > DDTREE_MAX_V) return DDTREE_ERR_UNSUPPORTED;
   return DDTREE_OK;
 }
@@ -77,26 +77,59 @@ DDT_API int ddtree_topk(const float* logits, int64_t row_stride, int L, int V, i
   return ddt_host::topk_launch(logits, row_stride, L, V, K, logp, token, ws, stream);
 }
 
-DDT_API int ddtree_build(const float* logp, const int32_t* token, int L, int K, int B,
-                         const int32_t* root_token, int32_t* parent, int32_t* depth,
-                         int32_t* node_token, float* score, uint32_t* anc, int mask_words,
-                         hipStream_t stream) {
-  if (L < 1 || K < 1 || B < 1) return DDTREE_ERR_INVALID_ARGUMENT;
+static int build_check(const float* logp, const int32_t* token, int L, int K, int B, int R,
+                       const int32_t* root_token, int32_t* parent, int32_t* depth,
+                       int32_t* node_token, uint32_t* anc, int mask_words) {
+  if (L < 1 || K < 1 || B < 1 || R < 1) return DDTREE_ERR_INVALID_ARGUMENT;
   if (L > DDTREE_MAX_L || K > DDTREE_MAX_K || B > DDTREE_MAX_B) return DDTREE_ERR_UNSUPPORTED;
+  if (R > DDTREE_MAX_REQ) return DDTREE_ERR_UNSUPPORTED;
   if ((int64_t)L * K > DDTREE_MAX_LK) return DDTREE_ERR_UNSUPPORTED;
   if (!enough_prefixes(L, K, B)) return DDTREE_ERR_INVALID_ARGUMENT;
   if (!logp || !token || !root_token || !parent || !depth || !node_token || !anc)
     return DDTREE_ERR_INVALID_ARGUMENT;
   if ((int64_t)mask_words * 32 < B + 1) return DDTREE_ERR_INVALID_ARGUMENT;
-  return ddt_host::build_launch(logp, token, L, K, B, root_token, parent, depth, node_token, score,
-                                anc, mask_words, stream);
+  return DDTREE_OK;
+}
+
+DDT_API int ddtree_build(const float* logp, const int32_t* token, int L, int K, int B,
+                         const int32_t* root_token, int32_t* parent, int32_t* depth,
+                         int32_t* node_token, float* score, uint32_t* anc, int mask_words,
+                         hipStream_t stream) {
+  const int st = build_check(logp, token, L, K, B, 1, root_token, parent, depth, node_token, anc,
+                             mask_words);
+  if (st) return st;
+  return ddt_host::build_launch(logp, token, L, K, B, 1, root_token, parent, depth, node_token,
+                                score, anc, mask_words, stream);
+}
+
+DDT_API int ddtree_build_batched(const float* logp, const int32_t* token, int L, int K, int B,
+                                 int R, const int32_t* root_token, int32_t* parent,
+                                 int32_t* depth, int32_t* node_token, float* score, uint32_t* anc,
+                                 int mask_words, hipStream_t stream) {
+  const int st = build_check(logp, token, L, K, B, R, root_token, parent, depth, node_token, anc,
+                             mask_words);
+  if (st) return st;
+  return ddt_host::build_launch(logp, token, L, K, B, R, root_token, parent, depth, node_token,
+                                score, anc, mask_words, stream);
 }
 
 DDT_API int ddtree_tree_attn_workspace_bytes(int N, int Hq, int Hkv, int D, int S, size_t* bytes) {
   if (!bytes) return DDTREE_ERR_INVALID_ARGUMENT;
   const int st = attn_check(N, Hq, Hkv, D, S);
   if (st) return st;
-  *bytes = ddt_host::attn_plan(N, Hq, Hkv, D, S).bytes;
+  *bytes = ddt_host::attn_plan(1, &S, N, Hq, Hkv, D).bytes;
+  return DDTREE_OK;
+}
+
+static int attn_args_check(const uint16_t* q, const uint16_t* k, const uint16_t* v, int S_cap,
+                           int N, float scale, const uint32_t* anc, int mask_words,
+                           const uint16_t* out) {
+  if (!q || !k || !v || !anc || !out) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return DDTREE_ERR_INVALID_ARGUMENT;
+  if (S_cap < N) return DDTREE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)mask_words * 32 < N) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f) || scale != scale || scale > 3.0e38f) return DDTREE_ERR_INVALID_ARGUMENT;
   return DDTREE_OK;
 }
 
@@ -104,18 +137,55 @@ DDT_API int ddtree_tree_attn(const uint16_t* q, const uint16_t* k, const uint16_
                              int S_cap, int N, int Hq, int Hkv, int D, float scale,
                              const uint32_t* anc, int mask_words, uint16_t* out, void* ws,
                              size_t ws_bytes, hipStream_t stream) {
-  const int st = attn_check(N, Hq, Hkv, D, S);
+  int st = attn_check(N, Hq, Hkv, D, S);
   if (st) return st;
-  if (!q || !k || !v || !anc || !out) return DDTREE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return DDTREE_ERR_INVALID_ARGUMENT;
+  st = attn_args_check(q, k, v, S_cap, N, scale, anc, mask_words, out);
+  if (st) return st;
   if ((int64_t)S + N > S_cap) return DDTREE_ERR_INVALID_ARGUMENT;
-  if ((int64_t)mask_words * 32 < N) return DDTREE_ERR_INVALID_ARGUMENT;
-  if (!(scale > 0.f) || scale != scale || scale > 3.0e38f) return DDTREE_ERR_INVALID_ARGUMENT;
-  const size_t need = ddt_host::attn_plan(N, Hq, Hkv, D, S).bytes;
+  const size_t need = ddt_host::attn_plan(1, &S, N, Hq, Hkv, D).bytes;
   if (need && (!ws || ws_bytes < need)) return DDTREE_ERR_WORKSPACE_TOO_SMALL;
-  return ddt_host::attn_launch(q, k, v, S, S_cap, N, Hq, Hkv, D, scale, anc, mask_words, out, ws,
-                               stream);
+  return ddt_host::attn_launch(q, k, v, 0, 1, &S, S_cap, N, Hq, Hkv, D, scale, anc, mask_words,
+                               out, ws, stream);
+}
+
+static int attn_batch_check(int R, const int32_t* S, int N, int Hq, int Hkv, int D) {
+  if (R < 1 || !S) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (R > DDTREE_MAX_REQ) return DDTREE_ERR_UNSUPPORTED;
+  for (int r = 0; r < R; ++r) {
+    const int st = attn_check(N, Hq, Hkv, D, S[r]);
+    if (st) return st;
+  }
+  return DDTREE_OK;
+}
+
+DDT_API int ddtree_tree_attn_batched_workspace_bytes(int R, const int32_t* S, int N, int Hq,
+                                                     int Hkv, int D, size_t* bytes) {
+  if (!bytes) return DDTREE_ERR_INVALID_ARGUMENT;
+  const int st = attn_batch_check(R, S, N, Hq, Hkv, D);
+  if (st) return st;
+  *bytes = ddt_host::attn_plan(R, S, N, Hq, Hkv, D).bytes;
+  return DDTREE_OK;
+}
+
+DDT_API int ddtree_tree_attn_batched(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     int64_t kv_req_stride, int R, const int32_t* S, int S_cap,
+                                     int N, int Hq, int Hkv, int D, float scale,
+                                     const uint32_t* anc, int mask_words, uint16_t* out,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = attn_batch_check(R, S, N, Hq, Hkv, D);
+  if (st) return st;
+  st = attn_args_check(q, k, v, S_cap, N, scale, anc, mask_words, out);
+  if (st) return st;
+  for (int r = 0; r < R; ++r)
+    if ((int64_t)S[r] + N > S_cap) return DDTREE_ERR_INVALID_ARGUMENT;
+  // Each request's K (and V) block [Hkv, S_cap, D] must fit in its stride,
+  // and the stride must keep 16-byte alignment.
+  if (R > 1 && (kv_req_stride < (int64_t)Hkv * S_cap * D || kv_req_stride % 8 != 0))
+    return DDTREE_ERR_INVALID_ARGUMENT;
+  const size_t need = ddt_host::attn_plan(R, S, N, Hq, Hkv, D).bytes;
+  if (need && (!ws || ws_bytes < need)) return DDTREE_ERR_WORKSPACE_TOO_SMALL;
+  return ddt_host::attn_launch(q, k, v, kv_req_stride, R, S, S_cap, N, Hq, Hkv, D, scale, anc,
+                               mask_words, out, ws, stream);
 }
 
 static int argmax_check(int dtype, int N, int V) {
@@ -179,25 +249,58 @@ DDT_API int ddtree_budget_select(const float* score, int B_max, int B_min, doubl
   return ddt_host::budget_launch(score, B_max, B_min, t0, t1, expected, budget, stream);
 }
 
+static int walk_check(const int32_t* parent, const int32_t* node_token, int N, int L, int R,
+                      const int32_t* target, int32_t* acc, int32_t* n_acc, int32_t* next_bonus) {
+  if (N < 1 || L < 1 || R < 1) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (L > DDTREE_MAX_L || N > DDTREE_MAX_B + 1 || R > DDTREE_MAX_REQ) return DDTREE_ERR_UNSUPPORTED;
+  if (!parent || !node_token || !target || !acc || !n_acc || !next_bonus)
+    return DDTREE_ERR_INVALID_ARGUMENT;
+  return DDTREE_OK;
+}
+
 DDT_API int ddtree_accept_walk(const int32_t* parent, const int32_t* node_token, int N, int L,
                                const int32_t* target_argmax, int32_t* acc, int32_t* n_acc,
                                int32_t* next_bonus, hipStream_t stream) {
-  if (N < 1 || L < 1) return DDTREE_ERR_INVALID_ARGUMENT;
-  if (L > DDTREE_MAX_L || N > DDTREE_MAX_B + 1) return DDTREE_ERR_UNSUPPORTED;
-  if (!parent || !node_token || !target_argmax || !acc || !n_acc || !next_bonus)
-    return DDTREE_ERR_INVALID_ARGUMENT;
-  return ddt_host::walk_launch(parent, node_token, N, L, target_argmax, acc, n_acc, next_bonus,
+  const int st = walk_check(parent, node_token, N, L, 1, target_argmax, acc, n_acc, next_bonus);
+  if (st) return st;
+  return ddt_host::walk_launch(parent, node_token, N, L, 1, target_argmax, acc, n_acc, next_bonus,
                                stream);
+}
+
+DDT_API int ddtree_accept_walk_batched(const int32_t* parent, const int32_t* node_token, int N,
+                                       int L, int R, const int32_t* target, int32_t* acc,
+                                       int32_t* n_acc, int32_t* next_bonus, hipStream_t stream) {
+  const int st = walk_check(parent, node_token, N, L, R, target, acc, n_acc, next_bonus);
+  if (st) return st;
+  return ddt_host::walk_launch(parent, node_token, N, L, R, target, acc, n_acc, next_bonus,
+                               stream);
+}
+
+static int compact_check(uint16_t* kv, int layers, int Hkv, int S_cap, int D, int R,
+                         const int32_t* S, int N, int L, const int32_t* acc,
+                         const int32_t* n_acc) {
+  if (layers < 1 || Hkv < 1 || N < 1 || L < 1 || R < 1) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (L > DDTREE_MAX_L || R > DDTREE_MAX_REQ) return DDTREE_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return DDTREE_ERR_UNSUPPORTED;
+  if (!kv || !acc || !n_acc || !S || !aligned16(kv)) return DDTREE_ERR_INVALID_ARGUMENT;
+  for (int r = 0; r < R; ++r)
+    if (S[r] < 0 || (int64_t)S[r] + N > S_cap) return DDTREE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)layers * 2 * Hkv > 0x7FFFFFFF) return DDTREE_ERR_UNSUPPORTED;
+  return DDTREE_OK;
 }
 
 DDT_API int ddtree_kv_compact(uint16_t* kv, int layers, int Hkv, int S_cap, int D, int S, int N,
                               int L, const int32_t* acc, const int32_t* n_acc,
                               hipStream_t stream) {
-  if (layers < 1 || Hkv < 1 || S < 0 || N < 1 || L < 1) return DDTREE_ERR_INVALID_ARGUMENT;
-  if (L > DDTREE_MAX_L) return DDTREE_ERR_UNSUPPORTED;
-  if (D != 64 && D != 128) return DDTREE_ERR_UNSUPPORTED;
-  if (!kv || !acc || !n_acc || !aligned16(kv)) return DDTREE_ERR_INVALID_ARGUMENT;
-  if ((int64_t)S + N > S_cap) return DDTREE_ERR_INVALID_ARGUMENT;
-  if ((int64_t)layers * 2 * Hkv > 0x7FFFFFFF) return DDTREE_ERR_UNSUPPORTED;
-  return ddt_host::compact_launch(kv, layers, Hkv, S_cap, D, S, acc, n_acc, stream);
+  const int st = compact_check(kv, layers, Hkv, S_cap, D, 1, &S, N, L, acc, n_acc);
+  if (st) return st;
+  return ddt_host::compact_launch(kv, layers, Hkv, S_cap, D, 1, &S, L, acc, n_acc, stream);
+}
+
+DDT_API int ddtree_kv_compact_batched(uint16_t* kv, int layers, int Hkv, int S_cap, int D, int R,
+                                      const int32_t* S, int N, int L, const int32_t* acc,
+                                      const int32_t* n_acc, hipStream_t stream) {
+  const int st = compact_check(kv, layers, Hkv, S_cap, D, R, S, N, L, acc, n_acc);
+  if (st) return st;
+  return ddt_host::compact_launch(kv, layers, Hkv, S_cap, D, R, S, L, acc, n_acc, stream);
 }

@@ -51,7 +51,11 @@
 // group, lane i receives element i%4 of the 4-element reads of lanes
 // 4e + i/4, so lanes point at (key 4h + e, dims 4*(lane%4) +
 // 16*((lane/16)%2)) and get 4 keys of one dim.
+#include <algorithm>
 #include <cstdlib>
+#include <cstring>
+#include <functional>
+#include <vector>
 
 #include "common.hpp"
 
@@ -398,10 +402,11 @@ __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void tree_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, int S, int S_cap, int N, int Hq, int Hkv,
-    float scale_log2, const uint32_t* __restrict__ anc, int W,
+    const uint16_t* __restrict__ v, int64_t kv_req_stride, ReqInts S_of, int S_cap, int N,
+    int Hq, int Hkv, float scale_log2, const uint32_t* __restrict__ anc, int W,
     uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int tiles, int splits, int sb_per_split, int wgs, int per_xcd) {
+    int tiles, ReqInts splits_of, ReqInts wg_end, ReqInts split_base, int sb_per_split, int wgs,
+    int per_xcd) {
   using C = Cfg<D>;
   // Two stages per operand, as distinct arrays: every read and every copy
   // below names a fixed array, so the compiler can tell that reading one
@@ -414,15 +419,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ float2 mlx[kWaves * 64];
   __shared__ uint32_t mrows[kRowsPerTile * kMaxMaskWords];
 
-  // Workgroup id -> position in the (kv-head, split, tile) order, one
-  // contiguous run per XCD. Ids past the work exit before any barrier.
-  const int idx = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-  if (idx >= wgs) return;
+  // Workgroup id -> position in the (request, kv-head, split, tile) order,
+  // one contiguous run per XCD. Ids past the work exit before any barrier.
+  const int idx0 = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (idx0 >= wgs) return;
+  // The request: the first whose workgroup range ends past idx0 (uniform).
+  int req = 0;
+  while (idx0 >= wg_end.v[req]) ++req;
+  const int idx = idx0 - (req ? wg_end.v[req - 1] : 0);
+  const int S = S_of.v[req];
+  const int splits = splits_of.v[req];
   const int tile = idx % tiles;
   const int gs = idx / tiles;
   const int split = gs % splits, g = gs / splits;
 
   const int G = Hq / Hkv, R = N * G;
+  q += (int64_t)req * N * Hq * D;
+  k += (int64_t)req * kv_req_stride;
+  v += (int64_t)req * kv_req_stride;
+  anc += (int64_t)req * N * W;
+  out += (int64_t)req * N * Hq * D;
   // The wave index is uniform: keep it (and all that derives from it, such
   // as the LDS destinations of the copies) in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -647,7 +663,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // (max, sum) pair per row. Non-temporal stores: the partials are read
     // once, by the combine kernel, and need not sit in L2 (whose dirty lines
     // would otherwise be written back at the end of the kernel).
-    const int64_t wb = ((int64_t)(split * Hkv + g) * tiles + tile) * kRowWaves + rw;
+    const int64_t wb =
+        ((int64_t)((split_base.v[req] + split) * Hkv + g) * tiles + tile) * kRowWaves + rw;
     f32x4* po = reinterpret_cast<f32x4*>(part_o) + (wb * C::DT + dt) * 4 * 64;
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd)
@@ -664,8 +681,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // batch issued before any is used, merged by a running maximum.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int N,
-    int Hq, int Hkv, int tiles, uint16_t* __restrict__ out) {
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, ReqInts splits_of,
+    ReqInts split_base, int N, int Hq, int Hkv, int tiles, uint16_t* __restrict__ out) {
+  // blockIdx.y is the request; one that ran as a single split wrote its
+  // output directly.
+  const int req = blockIdx.y;
+  const int splits = splits_of.v[req];
+  if (splits == 1) return;
+  out += (int64_t)req * N * Hq * D;
   constexpr int DT = D / 32;
   const int t = blockIdx.x * 256 + threadIdx.x;
   const int lane = t & 63, qd = (t >> 6) & 3;
@@ -687,7 +710,7 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(
     float4 x[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t wb = (int64_t)min(s0 + u, splits - 1) * WB + wbl;
+      const int64_t wb = (int64_t)(split_base.v[req] + min(s0 + u, splits - 1)) * WB + wbl;
       ml[u] = pml[wb * 32 + j];
       x[u] = po[((wb * DT + dt) * 4 + qd) * 64 + lane];
     }
@@ -724,7 +747,7 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(
   *reinterpret_cast<uint2*>(out + ((int64_t)node * Hq + hq) * D + d0) = pk;
 }
 
-// Workgroups the grid aims for: one per CU. DDTREE_ATTN_SLOTS overrides it
+// Workgroups resident at once: one per CU. DDTREE_ATTN_SLOTS overrides it
 // (for sweeps).
 int attn_slots() {
   static const int t = [] {
@@ -735,29 +758,166 @@ int attn_slots() {
   return t;
 }
 
+// DDTREE_ATTN_SBPS, when set, fixes the superblocks per split (for sweeps).
+int attn_sbps_override() {
+  static const int t = [] {
+    const char* s = std::getenv("DDTREE_ATTN_SBPS");
+    return s ? std::atoi(s) : 0;
+  }();
+  return t;
+}
+
+// Launch model constants, measured on the 30B verifier shape: one
+// superblock step, a workgroup's fixed work (set-up, merge, write), the
+// partials' HBM rate (bytes per microsecond) and the combine launch.
+constexpr double kStepUs = 1.4, kWgUs = 4.0, kPartBytesPerUs = 5.0e6, kCombineUs = 3.0;
+
+// Modelled time of the launch with `sbps` superblocks per split. The
+// workgroups run in id order; XCD x takes the contiguous id range the kernel
+// maps to it, and each of its CUs (slots / 8, one resident workgroup each)
+// takes the next workgroup when it frees up. A workgroup lasts its split's
+// superblocks times kStepUs plus kWgUs. Splitting adds the partials' round
+// trip through HBM and the combine launch. Returns early (with a value at
+// least `cap`) once the bound exceeds cap.
+double model_us(int nreq, const int* S, int N, int Hkv, int D, int tiles, int rows_pad, int sbps,
+                double cap) {
+  const int slots = attn_slots();
+  const int cus = std::max(1, slots / kXcds);
+  int64_t splits_total = 0;
+  double work = 0.0, longest = 0.0;
+  for (int r = 0; r < nreq; ++r) {
+    const int nsb = (S[r] + N + kSBK - 1) / kSBK;
+    const int sp = (nsb + sbps - 1) / sbps;
+    splits_total += sp;
+    work += (double)Hkv * tiles * (nsb * kStepUs + sp * kWgUs);
+    longest = std::max(longest, std::min(sbps, nsb) * kStepUs + kWgUs);
+  }
+  double extra = 0.0;
+  if (splits_total > nreq)
+    extra = (double)splits_total * Hkv * rows_pad * (D + 2) * 4 * 2 / kPartBytesPerUs + kCombineUs;
+  const double bound = std::max(work / slots, longest) + extra;
+  if (bound >= cap) return bound;
+  const int64_t wgs = splits_total * Hkv * tiles;
+  const int64_t per_xcd = (wgs + kXcds - 1) / kXcds;
+  double worst = 0.0;
+  std::vector<double> heap;
+  heap.reserve(cus);
+  int r = 0, g = 0, split = 0, tile = 0;  // the workgroup at id 0
+  for (int x = 0; x < kXcds; ++x) {
+    heap.assign(cus, 0.0);  // every CU free at time 0 (a min-heap of free times)
+    for (int64_t i = 0; i < per_xcd && x * per_xcd + i < wgs; ++i) {
+      const int nsb = (S[r] + N + kSBK - 1) / kSBK;
+      const double c = std::min(sbps, nsb - split * sbps) * kStepUs + kWgUs;
+      std::pop_heap(heap.begin(), heap.end(), std::greater<double>());
+      heap.back() += c;
+      std::push_heap(heap.begin(), heap.end(), std::greater<double>());
+      // Next id: tile fastest, then split, then kv-head, then request.
+      if (++tile == tiles) {
+        tile = 0;
+        if (++split == (nsb + sbps - 1) / sbps) {
+          split = 0;
+          if (++g == Hkv) {
+            g = 0;
+            ++r;
+          }
+        }
+      }
+    }
+    worst = std::max(worst, *std::max_element(heap.begin(), heap.end()));
+    if (worst + extra >= cap) return worst + extra;
+  }
+  return worst + extra;
+}
+
+struct PlanKey {
+  int nreq, N, Hq, Hkv, D, slots;
+  int S[DDTREE_MAX_REQ];
+};
+
+// Superblocks per split with the smallest modelled time; ties keep the
+// longer splits. Candidates: every count up to 64 superblocks, beyond that
+// the counts that cut the longest request into 1..64 equal splits. The
+// last choice is kept per thread, so the calls of one round (every layer,
+// same prefix lengths) plan once.
+int choose_sbps(int nreq, const int* S, int N, int Hq, int Hkv, int D, int tiles, int rows_pad) {
+  thread_local PlanKey last{};
+  thread_local int last_sbps = 0;
+  PlanKey key{};
+  key.nreq = nreq;
+  key.N = N;
+  key.Hq = Hq;
+  key.Hkv = Hkv;
+  key.D = D;
+  key.slots = attn_slots();
+  for (int r = 0; r < nreq; ++r) key.S[r] = S[r];
+  if (last_sbps > 0 && std::memcmp(&key, &last, sizeof(PlanKey)) == 0) return last_sbps;
+  int nsb_max = 1;
+  for (int r = 0; r < nreq; ++r) nsb_max = std::max(nsb_max, (S[r] + N + kSBK - 1) / kSBK);
+  std::vector<int> cand;
+  for (int c = 1; c <= std::min(nsb_max, 64); ++c) cand.push_back(c);
+  for (int k = 1; k <= 64; ++k) cand.push_back((nsb_max + k - 1) / k);
+  std::sort(cand.begin(), cand.end(), std::greater<int>());
+  cand.erase(std::unique(cand.begin(), cand.end()), cand.end());
+  int best = cand.front();
+  double best_us = model_us(nreq, S, N, Hkv, D, tiles, rows_pad, best, 1e300);
+  for (size_t i = 1; i < cand.size(); ++i) {
+    const double t = model_us(nreq, S, N, Hkv, D, tiles, rows_pad, cand[i], best_us);
+    if (t < best_us) {
+      best_us = t;
+      best = cand[i];
+    }
+  }
+  last = key;
+  last_sbps = best;
+  return best;
+}
+
 }  // namespace
 
 namespace ddt_host {
 
-AttnPlan attn_plan(int N, int Hq, int Hkv, int D, int S) {
-  AttnPlan p;
+AttnPlan attn_plan(int nreq, const int* S, int N, int Hq, int Hkv, int D) {
+  AttnPlan p{};
   const int G = Hq / Hkv, R = N * G;
+  p.nreq = nreq;
   p.tiles = (R + kRowsPerTile - 1) / kRowsPerTile;
   p.rows_pad = p.tiles * kRowsPerTile;
-  const int NSB = (S + N + kSBK - 1) / kSBK;
   const int per_split = Hkv * p.tiles;
-  // As many splits as keep the grid within one workgroup per CU; then even
-  // out the superblocks per split.
-  int splits = attn_slots() / per_split;
-  splits = splits < 1 ? 1 : (splits > NSB ? NSB : splits);
-  p.sb_per_split = (NSB + splits - 1) / splits;
-  p.splits = (NSB + p.sb_per_split - 1) / p.sb_per_split;
-  p.wgs = per_split * p.splits;
+  // One superblock count per split for every request, so requests with
+  // longer prefixes get proportionally more splits; chosen by simulating
+  // the launch (choose_sbps).
+  const int forced = attn_sbps_override();
+  int nsb_max = 1;
+  for (int r = 0; r < nreq; ++r) nsb_max = std::max(nsb_max, (S[r] + N + kSBK - 1) / kSBK);
+  p.sb_per_split = forced > 0 ? std::min(forced, nsb_max)
+                              : choose_sbps(nreq, S, N, Hq, Hkv, D, p.tiles, p.rows_pad);
+  int wg = 0, sp = 0;
+  p.any_split = false;
+  for (int r = 0; r < DDTREE_MAX_REQ; ++r) {
+    if (r < nreq) {
+      const int nsb = (S[r] + N + kSBK - 1) / kSBK;
+      const int splits = (nsb + p.sb_per_split - 1) / p.sb_per_split;
+      p.S.v[r] = S[r];
+      p.splits.v[r] = splits;
+      p.split_base.v[r] = sp;
+      sp += splits;
+      wg += per_split * splits;
+      p.wg_end.v[r] = wg;
+      p.any_split = p.any_split || splits > 1;
+    } else {
+      p.S.v[r] = 0;
+      p.splits.v[r] = 1;
+      p.split_base.v[r] = sp;
+      p.wg_end.v[r] = 0x7FFFFFFF;
+    }
+  }
+  p.total_splits = sp;
+  p.wgs = wg;
   p.per_xcd = (p.wgs + kXcds - 1) / kXcds;
-  if (p.splits == 1) {
+  if (!p.any_split) {
     p.part_o_off = p.part_ml_off = p.bytes = 0;
   } else {
-    const size_t rows = (size_t)p.splits * Hkv * p.rows_pad;
+    const size_t rows = (size_t)p.total_splits * Hkv * p.rows_pad;
     p.part_o_off = 0;
     p.part_ml_off = rows * D * sizeof(float);
     p.bytes = p.part_ml_off + rows * 2 * sizeof(float);
@@ -765,33 +925,35 @@ AttnPlan attn_plan(int N, int Hq, int Hkv, int D, int S) {
   return p;
 }
 
-int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int S, int S_cap, int N,
-                int Hq, int Hkv, int D, float scale, const uint32_t* anc, int W, uint16_t* out,
-                void* ws, hipStream_t stream) {
-  const AttnPlan p = attn_plan(N, Hq, Hkv, D, S);
-  float* po = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_o_off) : nullptr;
-  float* pml = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_ml_off) : nullptr;
+int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t kv_req_stride,
+                int nreq, const int* S, int S_cap, int N, int Hq, int Hkv, int D, float scale,
+                const uint32_t* anc, int W, uint16_t* out, void* ws, hipStream_t stream) {
+  const AttnPlan p = attn_plan(nreq, S, N, Hq, Hkv, D);
+  float* po = p.any_split ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_o_off) : nullptr;
+  float* pml = p.any_split ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_ml_off) : nullptr;
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(kXcds * p.per_xcd);
   if (D == 128) {
-    hipLaunchKernelGGL(tree_attn_kernel<128>, grid, dim3(kThreads), 0, stream, q, k, v, S, S_cap,
-                       N, Hq, Hkv, scale_log2, anc, W, out, po, pml, p.tiles, p.splits,
-                       p.sb_per_split, p.wgs, p.per_xcd);
+    hipLaunchKernelGGL(tree_attn_kernel<128>, grid, dim3(kThreads), 0, stream, q, k, v,
+                       kv_req_stride, p.S, S_cap, N, Hq, Hkv, scale_log2, anc, W, out, po, pml,
+                       p.tiles, p.splits, p.wg_end, p.split_base, p.sb_per_split, p.wgs,
+                       p.per_xcd);
   } else {
-    hipLaunchKernelGGL(tree_attn_kernel<64>, grid, dim3(kThreads), 0, stream, q, k, v, S, S_cap,
-                       N, Hq, Hkv, scale_log2, anc, W, out, po, pml, p.tiles, p.splits,
-                       p.sb_per_split, p.wgs, p.per_xcd);
+    hipLaunchKernelGGL(tree_attn_kernel<64>, grid, dim3(kThreads), 0, stream, q, k, v,
+                       kv_req_stride, p.S, S_cap, N, Hq, Hkv, scale_log2, anc, W, out, po, pml,
+                       p.tiles, p.splits, p.wg_end, p.split_base, p.sb_per_split, p.wgs,
+                       p.per_xcd);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return launch_status(e);
+  if (e != hipSuccess || !p.any_split) return launch_status(e);
   const int threads = Hkv * p.tiles * kRowWaves * (D / 32) * 4 * 64;
-  const dim3 cgrid((threads + 255) / 256);
+  const dim3 cgrid((threads + 255) / 256, nreq);
   if (D == 128) {
     hipLaunchKernelGGL(tree_attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, po, pml,
-                       p.splits, N, Hq, Hkv, p.tiles, out);
+                       p.splits, p.split_base, N, Hq, Hkv, p.tiles, out);
   } else {
     hipLaunchKernelGGL(tree_attn_combine_kernel<64>, cgrid, dim3(256), 0, stream, po, pml,
-                       p.splits, N, Hq, Hkv, p.tiles, out);
+                       p.splits, p.split_base, N, Hq, Hkv, p.tiles, out);
   }
   return launch_status(hipGetLastError());
 }

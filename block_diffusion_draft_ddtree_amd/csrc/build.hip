@@ -309,6 +309,19 @@ __global__ __launch_bounds__(kThreads) void build_kernel(
   __shared__ BuildLds s;
   const int t = threadIdx.x;
   const int LK = L * K;
+  // One workgroup per request: request r's table, root and outputs.
+  {
+    const int r = blockIdx.x;
+    const int N = B + 1;
+    logp += (int64_t)r * LK;
+    token += (int64_t)r * LK;
+    root_token += r;
+    parent_out += (int64_t)r * N;
+    depth_out += (int64_t)r * N;
+    tok_out += (int64_t)r * N;
+    if (score_out) score_out += (int64_t)r * N;
+    anc += (int64_t)r * N * W;
+  }
   for (int i = t; i < LK; i += kThreads) s.lp[i] = logp[i];
   if (t == 0) s.node[0] = 0u;  // the root
   __syncthreads();
@@ -348,13 +361,13 @@ __global__ __launch_bounds__(kThreads) void build_kernel(
 
 namespace ddt_host {
 
-int build_launch(const float* logp, const int32_t* token, int L, int K, int B,
+int build_launch(const float* logp, const int32_t* token, int L, int K, int B, int R,
                  const int32_t* root_token, int32_t* parent, int32_t* depth,
                  int32_t* node_token, float* score, uint32_t* anc, int W,
                  hipStream_t stream) {
   const int N = B + 1;
 #define DDT_BUILD(JJ)                                                              \
-  hipLaunchKernelGGL(build_kernel<JJ>, dim3(1), dim3(kThreads), 0, stream, logp,   \
+  hipLaunchKernelGGL(build_kernel<JJ>, dim3(R), dim3(kThreads), 0, stream, logp,   \
                      token, L, K, B, root_token, parent, depth, node_token, score, \
                      anc, W)
   if (N <= 64) DDT_BUILD(1);

@@ -5,6 +5,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ddtree.h"
+
+// One int per request, passed by value in the kernel arguments.
+struct ReqInts {
+  int v[DDTREE_MAX_REQ];
+};
+
 namespace ddt_host {
 
 int launch_status(hipError_t e);
@@ -18,21 +25,28 @@ TopkPlan topk_plan(int L, int V, int K);
 int topk_launch(const float* logits, int64_t stride, int L, int V, int K, float* logp,
                 int32_t* token, void* ws, hipStream_t stream);
 
-int build_launch(const float* logp, const int32_t* token, int L, int K, int B,
+int build_launch(const float* logp, const int32_t* token, int L, int K, int B, int R,
                  const int32_t* root_token, int32_t* parent, int32_t* depth,
                  int32_t* node_token, float* score, uint32_t* anc, int W, hipStream_t stream);
 
-// ddtree_tree_attn: grid shape and split-partial workspace.
+// ddtree_tree_attn: grid shape and split-partial workspace, for nreq
+// requests of N nodes each with their own prefix lengths.
 struct AttnPlan {
-  int tiles, rows_pad;       // 64-row query tiles per kv-head
-  int splits, sb_per_split;  // key range cut into splits of 128-key superblocks
-  int wgs, per_xcd;          // workgroups with work; grid = 8 * per_xcd
+  int nreq;
+  int tiles, rows_pad;    // 64-row query tiles per kv-head
+  int sb_per_split;       // 128-key superblocks per split, every request
+  ReqInts S, splits;      // per request: prefix length, splits of its key range
+  ReqInts wg_end;         // per request: end of its workgroup range
+  ReqInts split_base;     // per request: its first split in the partials
+  int total_splits;
+  bool any_split;         // some request runs more than one split
+  int wgs, per_xcd;       // workgroups with work; grid = 8 * per_xcd
   size_t part_o_off, part_ml_off, bytes;
 };
-AttnPlan attn_plan(int N, int Hq, int Hkv, int D, int S);
-int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int S, int S_cap, int N,
-                int Hq, int Hkv, int D, float scale, const uint32_t* anc, int W, uint16_t* out,
-                void* ws, hipStream_t stream);
+AttnPlan attn_plan(int nreq, const int* S, int N, int Hq, int Hkv, int D);
+int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t kv_req_stride,
+                int nreq, const int* S, int S_cap, int N, int Hq, int Hkv, int D, float scale,
+                const uint32_t* anc, int W, uint16_t* out, void* ws, hipStream_t stream);
 
 size_t argmax_workspace_bytes(int N, int V, int dtype_bytes);
 int argmax_launch(const void* logits, int bf16, int64_t row_stride, int N, int V, void* ws,
@@ -43,9 +57,10 @@ int sample_launch(const void* logits, int bf16, int64_t row_stride, int N, int V
 int budget_launch(const float* score, int B_max, int B_min, double t0, double t1,
                   float* expected, int32_t* budget, hipStream_t stream);
 
-int walk_launch(const int32_t* parent, const int32_t* tok, int N, int L, const int32_t* tgt,
-                int32_t* acc, int32_t* n_acc, int32_t* bonus, hipStream_t stream);
-int compact_launch(uint16_t* kv, int layers, int Hkv, int S_cap, int D, int S,
-                   const int32_t* acc, const int32_t* n_acc, hipStream_t stream);
+int walk_launch(const int32_t* parent, const int32_t* tok, int N, int L, int R,
+                const int32_t* tgt, int32_t* acc, int32_t* n_acc, int32_t* bonus,
+                hipStream_t stream);
+int compact_launch(uint16_t* kv, int layers, int Hkv, int S_cap, int D, int R, const int* S,
+                   int L, const int32_t* acc, const int32_t* n_acc, hipStream_t stream);
 
 }  // namespace ddt_host

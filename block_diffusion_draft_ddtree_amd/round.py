@@ -107,3 +107,52 @@ class DraftTreeRound:
             self.attn(layer, q, kv, S)
         self.walk(target_argmax)
         self.compact(kv, S)
+
+
+class BatchedDraftTreeRound:
+    """One round for R requests at once: each has its own drafter rows, tree,
+    prefix length S[r] and KV cache (kv: [R, layers, 2, Hkv, S_cap, D]); all
+    share L, V, K, B and the attention shape."""
+
+    def __init__(self, shape: RoundShape, S, device="cuda"):
+        s = shape
+        self.shape = s
+        self.R = len(S)
+        self.S = [int(x) for x in S]
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        R, N = self.R, s.N
+        self.logp = torch.empty((R * s.L, s.K), dtype=torch.float32, device=dev)
+        self.token = torch.empty((R * s.L, s.K), **i32)
+        self.ws_topk = bd.workspace(bd.ddtree_topk_workspace_bytes(R * s.L, s.V, s.K), dev)
+        self.root_token = torch.zeros(R, **i32)
+        self.attn_out = torch.empty((s.layers, R, N, s.Hq, s.D), dtype=torch.bfloat16, device=dev)
+        self.ws_attn = bd.workspace(
+            bd.ddtree_tree_attn_batched_workspace_bytes(self.S, N, s.Hq, s.Hkv, s.D), dev)
+        self.tree = None
+        self.walk_out = None
+
+    def topk(self, logits):
+        """logits fp32 [R * L, V]: request r's block positions at rows r * L ..."""
+        bd.ddtree_topk(logits, self.shape.K, self.logp, self.token, self.ws_topk)
+
+    def build(self):
+        s = self.shape
+        self.tree = bd.ddtree_build_batched(self.logp.view(self.R, s.L, s.K),
+                                            self.token.view(self.R, s.L, s.K), s.B,
+                                            self.root_token, s.W)
+
+    def attn(self, layer: int, q, kv):
+        """q bf16 [R, N, Hq, D] for this layer; kv [R, layers, 2, Hkv, S_cap, D]."""
+        bd.ddtree_tree_attn_batched(q, kv, layer, self.S, self.tree[4], out=self.attn_out[layer],
+                                    ws=self.ws_attn)
+
+    def walk(self, target):
+        """target int32 [R, N]: the target's token per node of every request."""
+        parent, _, node_token, _, _ = self.tree
+        self.walk_out = bd.ddtree_accept_walk_batched(parent, node_token, self.shape.L, target)
+        return self.walk_out
+
+    def compact(self, kv):
+        acc, n_acc, _ = self.walk_out
+        bd.ddtree_kv_compact_batched(kv, self.S, self.shape.N, self.shape.L, acc, n_acc)

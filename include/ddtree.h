@@ -11,6 +11,8 @@
  *   ddtree_budget_select  cost-aware node budget from the build's scores
  *   ddtree_accept_walk  greedy walk of the target's argmax down the tree
  *   ddtree_kv_compact   in-place gather of the accepted path's K/V rows
+ *   ..._batched         the same for R requests in one call (a tree and a
+ *                       prefix length per request)
  *
  * Sources (the web pages on DDTree; cited by page title and section):
  *   [DD]  "DDTree Deep Dive: Algorithm, Code, and Engineering Philosophy of
@@ -25,9 +27,10 @@
  * - Every pointer is a DEVICE pointer unless its comment says "host".
  * - bf16 tensors are passed as uint16_t bit patterns (IEEE bfloat16).
  * - All arrays are dense row-major with the shapes given; the caller owns
- *   every buffer. The library allocates nothing, keeps no pointer after a
- *   call returns and holds no mutable global state: calls are re-entrant and
- *   thread-safe.
+ *   every buffer. The library allocates nothing and keeps no pointer after
+ *   a call returns; its only state is a per-thread cache of the last
+ *   attention launch plan (a pure function of the shapes and prefix
+ *   lengths), so calls are re-entrant and thread-safe.
  * - Every call validates its arguments on the host first; on error it
  *   returns a non-zero ddtree_status and enqueues nothing. On success the
  *   work is enqueued on `stream` (may be 0 = null stream) and the call
@@ -66,6 +69,7 @@ typedef enum ddtree_status {
 #define DDTREE_MAX_B 1024      /* node budget (the pages sweep 16..1024)     */
 #define DDTREE_MAX_LK 32768    /* L * K: the whole top-K table sits in LDS   */
 #define DDTREE_MAX_V 4194304   /* vocabulary (1024 chunks of 4096 logits)    */
+#define DDTREE_MAX_REQ 64      /* requests in one batched call               */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* ddtree_status_string(int status);
@@ -81,9 +85,12 @@ int ddtree_version(void);
  * position matter); [AH] Key Concepts (node scores are sums of log-probs).
  *
  * logits      fp32 [L, row_stride]; row i holds V logits of block position i
- *             (0-based). Values must be finite.
+ *             (0-based). Values must be finite. Rows are independent: for R
+ *             requests pass their rows stacked (request r's block positions
+ *             at rows r * L_req ... r * L_req + L_req - 1), and the output
+ *             is the [R, L_req, K] table ddtree_build_batched reads.
  * row_stride  elements between rows, >= V.
- * L, V, K     1 <= L <= DDTREE_MAX_L, 1 <= V <= DDTREE_MAX_V,
+ * L, V, K     1 <= L <= DDTREE_MAX_L * DDTREE_MAX_REQ, 1 <= V <= DDTREE_MAX_V,
  *             1 <= K <= min(V, DDTREE_MAX_K).
  * logp        out fp32 [L, K]: log q_i of the selected tokens, rank order.
  * token       out int32 [L, K]: their token ids.
@@ -131,6 +138,16 @@ int ddtree_build(const float* logp, const int32_t* token, int L, int K, int B,
                  int32_t* node_token, float* score, uint32_t* anc,
                  int mask_words, hipStream_t stream);
 
+/* ddtree_build_batched -- ddtree_build for R requests (one workgroup each),
+ * 1 <= R <= DDTREE_MAX_REQ, all with the same L, K, B: logp and token are
+ * [R, L, K], root_token [R], parent/depth/node_token/score [R, B + 1] and
+ * anc [R, B + 1, mask_words]; request r's slices are exactly what
+ * ddtree_build would produce from its own slices. */
+int ddtree_build_batched(const float* logp, const int32_t* token, int L, int K, int B, int R,
+                         const int32_t* root_token, int32_t* parent, int32_t* depth,
+                         int32_t* node_token, float* score, uint32_t* anc, int mask_words,
+                         hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * ddtree_tree_attn -- ancestor-only tree attention of one layer (GQA, bf16).
  *
@@ -164,6 +181,31 @@ int ddtree_tree_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      float scale, const uint32_t* anc, int mask_words,
                      uint16_t* out, void* ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/* ddtree_tree_attn_batched -- ddtree_tree_attn for R requests in one launch
+ * (1 <= R <= DDTREE_MAX_REQ), each with its own tree and its own prefix
+ * length; all share N, Hq, Hkv, D and S_cap.
+ *
+ * q, out      bf16 [R, N, Hq, D].
+ * k, v        request r's [Hkv, S_cap, D] block starts kv_req_stride
+ *             elements after request r - 1's (a multiple of 8, and at least
+ *             Hkv * S_cap * D when R > 1); e.g. a cache laid out
+ *             [R][layers][2][Hkv][S_cap][D] passes k = its layer's K block of
+ *             request 0 and kv_req_stride = layers * 2 * Hkv * S_cap * D.
+ * S           host int32 [R]: request r's prefix length, S[r] + N <= S_cap.
+ * anc         uint32 [R, N, mask_words].
+ * ws          scratch of at least ddtree_tree_attn_batched_workspace_bytes()
+ *             for the same R, S, N, Hq, Hkv, D.
+ * The key range of every request is cut into splits of one common length,
+ * so the launch's workgroups follow the total work; request r's output
+ * equals ddtree_tree_attn on its own slices. */
+int ddtree_tree_attn_batched_workspace_bytes(int R, const int32_t* S /* host */, int N, int Hq,
+                                             int Hkv, int D, size_t* bytes /* host */);
+int ddtree_tree_attn_batched(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             int64_t kv_req_stride, int R, const int32_t* S /* host */,
+                             int S_cap, int N, int Hq, int Hkv, int D, float scale,
+                             const uint32_t* anc, int mask_words, uint16_t* out, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * ddtree_target_argmax -- the target's greedy choice after every tree node.
@@ -278,6 +320,13 @@ int ddtree_accept_walk(const int32_t* parent, const int32_t* node_token, int N,
                        int L, const int32_t* target_argmax, int32_t* acc,
                        int32_t* n_acc, int32_t* next_bonus, hipStream_t stream);
 
+/* ddtree_accept_walk_batched -- ddtree_accept_walk for R requests (one wave
+ * each), 1 <= R <= DDTREE_MAX_REQ: parent, node_token and target are
+ * [R, N], acc [R, L + 1], n_acc and next_bonus [R]. */
+int ddtree_accept_walk_batched(const int32_t* parent, const int32_t* node_token, int N, int L,
+                               int R, const int32_t* target, int32_t* acc, int32_t* n_acc,
+                               int32_t* next_bonus, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * ddtree_kv_compact -- keep only the accepted path in the KV cache, in place.
  *
@@ -297,6 +346,14 @@ int ddtree_accept_walk(const int32_t* parent, const int32_t* node_token, int N,
 int ddtree_kv_compact(uint16_t* kv, int layers, int Hkv, int S_cap, int D,
                       int S, int N, int L, const int32_t* acc,
                       const int32_t* n_acc, hipStream_t stream);
+
+/* ddtree_kv_compact_batched -- ddtree_kv_compact for R requests in one
+ * launch, 1 <= R <= DDTREE_MAX_REQ: kv is [R][layers][2][Hkv][S_cap][D]
+ * (16-byte aligned), S a host int32 [R] of prefix lengths (S[r] + N <=
+ * S_cap), acc [R, L + 1] and n_acc [R] from ddtree_accept_walk_batched. */
+int ddtree_kv_compact_batched(uint16_t* kv, int layers, int Hkv, int S_cap, int D, int R,
+                              const int32_t* S /* host */, int N, int L, const int32_t* acc,
+                              const int32_t* n_acc, hipStream_t stream);
 
 #ifdef __cplusplus
 }

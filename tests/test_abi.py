@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(bd.EXPORTS)
@@ -48,7 +48,7 @@ def test_workspace_queries(lib):
     assert bd.ddtree_tree_attn_workspace_bytes(65, 32, 4, 128, 4096) > 0
     # a single split needs no workspace
     assert bd.ddtree_tree_attn_workspace_bytes(1, 1, 1, 64, 0) == 0
-    for args in [(0, 10, 1), (1, 10, 11), (33, 10, 1), (1, 5000, 1025)]:
+    for args in [(0, 10, 1), (1, 10, 11), (32 * 64 + 1, 10, 1), (1, 5000, 1025)]:
         with pytest.raises(bd.DDTreeError):
             bd.ddtree_topk_workspace_bytes(*args)
     with pytest.raises(bd.DDTreeError):
@@ -70,7 +70,8 @@ def test_topk_validation(lib):
     assert f(None, 1000, 4, 1000, 8, P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
     assert f(P(FAKE), 999, 4, 1000, 8, P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
     assert f(P(FAKE), 1000, 4, 1000, 1001, P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
-    assert f(P(FAKE), 1000, 33, 1000, 8, P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == bd.DDTREE_ERR_UNSUPPORTED
+    # Rows: up to DDTREE_MAX_L block positions of up to DDTREE_MAX_REQ requests.
+    assert f(P(FAKE), 1000, 32 * 64 + 1, 1000, 8, P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == bd.DDTREE_ERR_UNSUPPORTED
 
 
 def test_build_validation(lib):
@@ -169,3 +170,42 @@ def test_budget_select_validation(lib):
     for t0, t1 in ((0.0, 0.0), (-1.0, 0.1), (1.0, -0.1), (float("nan"), 0.1), (float("inf"), 0.1),
                    (1.0, float("inf"))):
         assert f(P(FAKE), 64, 1, t0, t1, None, P(FAKE), None) == E, (t0, t1)
+
+
+def test_batched_validation(lib):
+    E, U = bd.DDTREE_ERR_INVALID_ARGUMENT, bd.DDTREE_ERR_UNSUPPORTED
+    b = lib.ddtree_build_batched
+    args = [P(FAKE), P(FAKE), 16, 64, 64, 4, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE), 3, None]
+    a = list(args); a[5] = 0
+    assert b(*a) == E
+    a = list(args); a[5] = 65
+    assert b(*a) == U
+    a = list(args); a[6] = None
+    assert b(*a) == E
+    w = lib.ddtree_accept_walk_batched
+    assert w(P(FAKE), P(FAKE), 65, 16, 0, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == E
+    assert w(P(FAKE), P(FAKE), 65, 16, 65, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == U
+    S = bd._host_ints([4096, 100, 0])
+    nb = ctypes.c_size_t(0)
+    q = lib.ddtree_tree_attn_batched_workspace_bytes
+    assert q(3, S, 65, 32, 4, 128, ctypes.byref(nb)) == 0 and nb.value > 0
+    assert q(0, S, 65, 32, 4, 128, ctypes.byref(nb)) == E
+    assert q(65, S, 65, 32, 4, 128, ctypes.byref(nb)) == U
+    assert q(3, None, 65, 32, 4, 128, ctypes.byref(nb)) == E
+    assert q(3, bd._host_ints([1, -1, 2]), 65, 32, 4, 128, ctypes.byref(nb)) == E
+    t = lib.ddtree_tree_attn_batched
+    stride = 48 * 2 * 4 * 4200 * 128
+    ok = [P(FAKE), P(FAKE), P(FAKE), stride, 3, S, 4200, 65, 32, 4, 128, 0.088, P(FAKE), 3,
+          P(FAKE), P(FAKE), 1 << 30, None]
+    x = list(ok); x[6] = 4160  # 4096 + 65 > S_cap
+    assert t(*x) == E
+    x = list(ok); x[3] = 4 * 4200 * 128 - 8  # stride below one request's block
+    assert t(*x) == E
+    x = list(ok); x[3] = stride + 4  # stride breaks 16-byte alignment
+    assert t(*x) == E
+    x = list(ok); x[16] = 0
+    assert t(*x) == bd.DDTREE_ERR_WORKSPACE_TOO_SMALL
+    c = lib.ddtree_kv_compact_batched
+    assert c(P(FAKE), 48, 4, 4160, 128, 3, S, 65, 16, P(FAKE), P(FAKE), None) == E
+    assert c(P(FAKE), 48, 4, 4200, 128, 3, None, 65, 16, P(FAKE), P(FAKE), None) == E
+    assert c(P(FAKE), 48, 4, 4200, 128, 65, S, 65, 16, P(FAKE), P(FAKE), None) == U
