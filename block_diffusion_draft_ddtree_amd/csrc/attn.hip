@@ -399,14 +399,23 @@ __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
   }
 }
 
+// Splits of a request's key range and its first split in the partials,
+// from its prefix length and the end of the previous request's workgroups.
+__device__ __forceinline__ int req_splits(int S, int N, int sb_per_split) {
+  return ((S + N + kSBK - 1) / kSBK + sb_per_split - 1) / sb_per_split;
+}
+
+// The work of one workgroup: position idx in its request's (kv-head, split,
+// tile) order; q, k, v, anc and out already point at the request's slices;
+// part_base = the request's first split times Hkv (its partial tiles start
+// at part_base * tiles * kRowWaves).
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void tree_attn_kernel(
+__device__ __forceinline__ void attn_workgroup(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, int64_t kv_req_stride, ReqInts S_of, int S_cap, int N,
-    int Hq, int Hkv, float scale_log2, const uint32_t* __restrict__ anc, int W,
-    uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int tiles, ReqInts splits_of, ReqInts wg_end, ReqInts split_base, int sb_per_split, int wgs,
-    int per_xcd) {
+    const uint16_t* __restrict__ v, int S, int S_cap, int N, int Hq, int Hkv, float scale_log2,
+    const uint32_t* __restrict__ anc, int W, uint16_t* __restrict__ out,
+    float* __restrict__ part_o, float* __restrict__ part_ml, int tiles, int splits,
+    int part_base, int sb_per_split, int idx) {
   using C = Cfg<D>;
   // Two stages per operand, as distinct arrays: every read and every copy
   // below names a fixed array, so the compiler can tell that reading one
@@ -419,26 +428,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ float2 mlx[kWaves * 64];
   __shared__ uint32_t mrows[kRowsPerTile * kMaxMaskWords];
 
-  // Workgroup id -> position in the (request, kv-head, split, tile) order,
-  // one contiguous run per XCD. Ids past the work exit before any barrier.
-  const int idx0 = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-  if (idx0 >= wgs) return;
-  // The request: the first whose workgroup range ends past idx0 (uniform).
-  int req = 0;
-  while (idx0 >= wg_end.v[req]) ++req;
-  const int idx = idx0 - (req ? wg_end.v[req - 1] : 0);
-  const int S = S_of.v[req];
-  const int splits = splits_of.v[req];
   const int tile = idx % tiles;
   const int gs = idx / tiles;
   const int split = gs % splits, g = gs / splits;
 
   const int G = Hq / Hkv, R = N * G;
-  q += (int64_t)req * N * Hq * D;
-  k += (int64_t)req * kv_req_stride;
-  v += (int64_t)req * kv_req_stride;
-  anc += (int64_t)req * N * W;
-  out += (int64_t)req * N * Hq * D;
   // The wave index is uniform: keep it (and all that derives from it, such
   // as the LDS destinations of the copies) in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -664,7 +658,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // once, by the combine kernel, and need not sit in L2 (whose dirty lines
     // would otherwise be written back at the end of the kernel).
     const int64_t wb =
-        ((int64_t)((split_base.v[req] + split) * Hkv + g) * tiles + tile) * kRowWaves + rw;
+        ((int64_t)(part_base + split * Hkv + g) * tiles + tile) * kRowWaves + rw;
     f32x4* po = reinterpret_cast<f32x4*>(part_o) + (wb * C::DT + dt) * 4 * 64;
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd)
@@ -675,20 +669,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
+// Workgroup id -> position in the (request, kv-head, split, tile) order,
+// one contiguous run per XCD. Ids past the work exit before any barrier.
+__device__ __forceinline__ int xcd_run_index(int per_xcd) {
+  return (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+}
+
+// One request: its values are plain arguments.
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void tree_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int S, int S_cap, int N, int Hq, int Hkv, float scale_log2,
+    const uint32_t* __restrict__ anc, int W, uint16_t* __restrict__ out,
+    float* __restrict__ part_o, float* __restrict__ part_ml, int tiles, int splits,
+    int sb_per_split, int wgs, int per_xcd) {
+  const int idx = xcd_run_index(per_xcd);
+  if (idx >= wgs) return;
+  attn_workgroup<D>(q, k, v, S, S_cap, N, Hq, Hkv, scale_log2, anc, W, out, part_o, part_ml,
+                    tiles, splits, 0, sb_per_split, idx);
+}
+
+// Several requests: prefix lengths and cumulative workgroup ends per
+// request; request r's slices start r strides into q, anc, out and
+// kv_req_stride elements into k and v.
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void tree_attn_batched_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int64_t kv_req_stride, ReqInts S_of, ReqInts wg_end,
+    int S_cap, int N, int Hq, int Hkv, float scale_log2, const uint32_t* __restrict__ anc, int W,
+    uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int tiles, int sb_per_split, int wgs, int per_xcd) {
+  const int idx0 = xcd_run_index(per_xcd);
+  if (idx0 >= wgs) return;
+  int req = 0;  // the first request whose workgroups end past idx0 (uniform)
+  while (idx0 >= wg_end.v[req]) ++req;
+  const int wg0 = req ? wg_end.v[req - 1] : 0;
+  const int S = S_of.v[req];
+  const int64_t qo = (int64_t)req * N * Hq * D;
+  attn_workgroup<D>(q + qo, k + req * kv_req_stride, v + req * kv_req_stride, S, S_cap, N, Hq,
+                    Hkv, scale_log2, anc + (int64_t)req * N * W, W, out + qo, part_o, part_ml,
+                    tiles, req_splits(S, N, sb_per_split), wg0 / tiles, sb_per_split,
+                    idx0 - wg0);
+}
+
 // Merge the per-split partials. One thread per float4 of a partial tile
 // (the same slot in every split), so each load instruction of a wave reads
 // 1 KB contiguously; the splits are taken 8 at a time with every load of a
 // batch issued before any is used, merged by a running maximum.
 template <int D>
-__global__ __launch_bounds__(256) void tree_attn_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, ReqInts splits_of,
-    ReqInts split_base, int N, int Hq, int Hkv, int tiles, uint16_t* __restrict__ out) {
-  // blockIdx.y is the request; one that ran as a single split wrote its
-  // output directly.
-  const int req = blockIdx.y;
-  const int splits = splits_of.v[req];
-  if (splits == 1) return;
-  out += (int64_t)req * N * Hq * D;
+__device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
+                                             const float* __restrict__ part_ml, int splits,
+                                             int split_base, int N, int Hq, int Hkv, int tiles,
+                                             uint16_t* __restrict__ out) {
   constexpr int DT = D / 32;
   const int t = blockIdx.x * 256 + threadIdx.x;
   const int lane = t & 63, qd = (t >> 6) & 3;
@@ -710,7 +742,7 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(
     float4 x[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t wb = (int64_t)(split_base.v[req] + min(s0 + u, splits - 1)) * WB + wbl;
+      const int64_t wb = (int64_t)(split_base + min(s0 + u, splits - 1)) * WB + wbl;
       ml[u] = pml[wb * 32 + j];
       x[u] = po[((wb * DT + dt) * 4 + qd) * 64 + lane];
     }
@@ -745,6 +777,28 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(
   pk.x = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
   pk.y = (uint32_t)f32_to_bf16_rne(acc.z * inv) | ((uint32_t)f32_to_bf16_rne(acc.w * inv) << 16);
   *reinterpret_cast<uint2*>(out + ((int64_t)node * Hq + hq) * D + d0) = pk;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void tree_attn_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int N,
+    int Hq, int Hkv, int tiles, uint16_t* __restrict__ out) {
+  combine_rows<D>(part_o, part_ml, splits, 0, N, Hq, Hkv, tiles, out);
+}
+
+// blockIdx.y is the request; one that ran as a single split wrote its
+// output directly.
+template <int D>
+__global__ __launch_bounds__(256) void tree_attn_batched_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, ReqInts S_of,
+    ReqInts wg_end, int sb_per_split, int N, int Hq, int Hkv, int tiles,
+    uint16_t* __restrict__ out) {
+  const int req = blockIdx.y;
+  const int splits = req_splits(S_of.v[req], N, sb_per_split);
+  if (splits == 1) return;
+  const int split_base = req ? wg_end.v[req - 1] / (Hkv * tiles) : 0;
+  combine_rows<D>(part_o, part_ml, splits, split_base, N, Hq, Hkv, tiles,
+                  out + (int64_t)req * N * Hq * D);
 }
 
 // Workgroups resident at once: one per CU. DDTREE_ATTN_SLOTS overrides it
@@ -933,29 +987,47 @@ int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t
   float* pml = p.any_split ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_ml_off) : nullptr;
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(kXcds * p.per_xcd);
-  if (D == 128) {
-    hipLaunchKernelGGL(tree_attn_kernel<128>, grid, dim3(kThreads), 0, stream, q, k, v,
-                       kv_req_stride, p.S, S_cap, N, Hq, Hkv, scale_log2, anc, W, out, po, pml,
-                       p.tiles, p.splits, p.wg_end, p.split_base, p.sb_per_split, p.wgs,
-                       p.per_xcd);
+  if (nreq == 1) {
+    const int splits = p.splits.v[0];
+    if (D == 128)
+      hipLaunchKernelGGL(tree_attn_kernel<128>, grid, dim3(kThreads), 0, stream, q, k, v, S[0],
+                         S_cap, N, Hq, Hkv, scale_log2, anc, W, out, po, pml, p.tiles, splits,
+                         p.sb_per_split, p.wgs, p.per_xcd);
+    else
+      hipLaunchKernelGGL(tree_attn_kernel<64>, grid, dim3(kThreads), 0, stream, q, k, v, S[0],
+                         S_cap, N, Hq, Hkv, scale_log2, anc, W, out, po, pml, p.tiles, splits,
+                         p.sb_per_split, p.wgs, p.per_xcd);
   } else {
-    hipLaunchKernelGGL(tree_attn_kernel<64>, grid, dim3(kThreads), 0, stream, q, k, v,
-                       kv_req_stride, p.S, S_cap, N, Hq, Hkv, scale_log2, anc, W, out, po, pml,
-                       p.tiles, p.splits, p.wg_end, p.split_base, p.sb_per_split, p.wgs,
-                       p.per_xcd);
+    if (D == 128)
+      hipLaunchKernelGGL(tree_attn_batched_kernel<128>, grid, dim3(kThreads), 0, stream, q, k, v,
+                         kv_req_stride, p.S, p.wg_end, S_cap, N, Hq, Hkv, scale_log2, anc, W,
+                         out, po, pml, p.tiles, p.sb_per_split, p.wgs, p.per_xcd);
+    else
+      hipLaunchKernelGGL(tree_attn_batched_kernel<64>, grid, dim3(kThreads), 0, stream, q, k, v,
+                         kv_req_stride, p.S, p.wg_end, S_cap, N, Hq, Hkv, scale_log2, anc, W,
+                         out, po, pml, p.tiles, p.sb_per_split, p.wgs, p.per_xcd);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.any_split) return launch_status(e);
   const int threads = Hkv * p.tiles * kRowWaves * (D / 32) * 4 * 64;
   const dim3 cgrid((threads + 255) / 256, nreq);
-  if (D == 128) {
-    hipLaunchKernelGGL(tree_attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, po, pml,
-                       p.splits, p.split_base, N, Hq, Hkv, p.tiles, out);
+  if (nreq == 1) {
+    if (D == 128)
+      hipLaunchKernelGGL(tree_attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, po, pml,
+                         p.splits.v[0], N, Hq, Hkv, p.tiles, out);
+    else
+      hipLaunchKernelGGL(tree_attn_combine_kernel<64>, cgrid, dim3(256), 0, stream, po, pml,
+                         p.splits.v[0], N, Hq, Hkv, p.tiles, out);
   } else {
-    hipLaunchKernelGGL(tree_attn_combine_kernel<64>, cgrid, dim3(256), 0, stream, po, pml,
-                       p.splits, p.split_base, N, Hq, Hkv, p.tiles, out);
+    if (D == 128)
+      hipLaunchKernelGGL(tree_attn_batched_combine_kernel<128>, cgrid, dim3(256), 0, stream, po,
+                         pml, p.S, p.wg_end, p.sb_per_split, N, Hq, Hkv, p.tiles, out);
+    else
+      hipLaunchKernelGGL(tree_attn_batched_combine_kernel<64>, cgrid, dim3(256), 0, stream, po,
+                         pml, p.S, p.wg_end, p.sb_per_split, N, Hq, Hkv, p.tiles, out);
   }
   return launch_status(hipGetLastError());
 }
+
 
 }  // namespace ddt_host
