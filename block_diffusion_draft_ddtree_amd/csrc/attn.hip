@@ -111,6 +111,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 values rounded to fp16 (nearest even), low half first; and back.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const _Float16 x = (_Float16)a, y = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
 // v_permlane32_swap of a value with itself leaves the low half's values in
 // one result and the high half's in the other, on every lane: their max is
 // the max over lanes j and j + 32.
@@ -653,17 +666,23 @@ __device__ __forceinline__ void attn_workgroup(
       *reinterpret_cast<uint2*>(orow + d0) = pk;
     }
   } else {
-    // Partial tile wb of this split: [DT][4][64 lanes] float4 plus one
-    // (max, sum) pair per row. Non-temporal stores: the partials are read
-    // once, by the combine kernel, and need not sit in L2 (whose dirty lines
-    // would otherwise be written back at the end of the kernel).
+    // Partial tile wb of this split: the split's output normalised by its
+    // own sum, [DT][4][64 lanes] x 4 fp16, plus one fp32 (max, sum) pair
+    // per row. Normalised values lie within the V rows' range, so fp16
+    // keeps them to 2^-11 relative, well inside the final bf16 rounding;
+    // half the bytes of fp32 partials to write here and read back in the
+    // combine. Non-temporal stores: the partials are read once, by the
+    // combine kernel, and need not sit in L2 (whose dirty lines would
+    // otherwise be written back at the end of the kernel).
     const int64_t wb =
         ((int64_t)(part_base + split * Hkv + g) * tiles + tile) * kRowWaves + rw;
-    f32x4* po = reinterpret_cast<f32x4*>(part_o) + (wb * C::DT + dt) * 4 * 64;
+    const float inv = L > 0.f ? 1.0f / L : 0.f;  // a split may see no key of a row
+    u32x2* po = reinterpret_cast<u32x2*>(part_o) + (wb * C::DT + dt) * 4 * 64;
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd)
       __builtin_nontemporal_store(
-          f32x4{acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]},
+          u32x2{pack_f16x2(acc[4 * qd] * inv, acc[4 * qd + 1] * inv),
+                pack_f16x2(acc[4 * qd + 2] * inv, acc[4 * qd + 3] * inv)},
           po + qd * 64 + lane);
     if (dt == 0 && h == 0) reinterpret_cast<float2*>(part_ml)[wb * 32 + j] = make_float2(M, L);
   }
@@ -733,18 +752,18 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
   const int j = lane & 31, h = lane >> 5;
   const int rho = tile * kRowsPerTile + rw * 32 + j;
   if (rho >= R) return;
-  const float4* po = reinterpret_cast<const float4*>(part_o);
+  const uint2* po = reinterpret_cast<const uint2*>(part_o);
   const float2* pml = reinterpret_cast<const float2*>(part_ml);
   float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < splits; s0 += 8) {
     float2 ml[8];
-    float4 x[8];
+    uint2 xh[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int64_t wb = (int64_t)(split_base + min(s0 + u, splits - 1)) * WB + wbl;
       ml[u] = pml[wb * 32 + j];
-      x[u] = po[((wb * DT + dt) * 4 + qd) * 64 + lane];
+      xh[u] = po[((wb * DT + dt) * 4 + qd) * 64 + lane];
     }
     float bm = M;
 #pragma unroll
@@ -760,12 +779,13 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (s0 + u < splits) {
-        const float w = __builtin_amdgcn_exp2f(ml[u].x - bmu);
-        L += w * ml[u].y;
-        acc.x += w * x[u].x;
-        acc.y += w * x[u].y;
-        acc.z += w * x[u].z;
-        acc.w += w * x[u].w;
+        // The split's weight: its sum rescaled to the running maximum.
+        const float w = __builtin_amdgcn_exp2f(ml[u].x - bmu) * ml[u].y;
+        L += w;
+        acc.x += w * f16_lo(xh[u].x);
+        acc.y += w * f16_hi(xh[u].x);
+        acc.z += w * f16_lo(xh[u].y);
+        acc.w += w * f16_hi(xh[u].y);
       }
     }
     M = bm;
@@ -848,7 +868,7 @@ double model_us(int nreq, const int* S, int N, int Hkv, int D, int tiles, int ro
   }
   double extra = 0.0;
   if (splits_total > nreq)
-    extra = (double)splits_total * Hkv * rows_pad * (D + 2) * 4 * 2 / kPartBytesPerUs + kCombineUs;
+    extra = (double)splits_total * Hkv * rows_pad * (2 * D + 8) * 2 / kPartBytesPerUs + kCombineUs;
   const double bound = std::max(work / slots, longest) + extra;
   if (bound >= cap) return bound;
   const int64_t wgs = splits_total * Hkv * tiles;
@@ -973,7 +993,7 @@ AttnPlan attn_plan(int nreq, const int* S, int N, int Hq, int Hkv, int D) {
   } else {
     const size_t rows = (size_t)p.total_splits * Hkv * p.rows_pad;
     p.part_o_off = 0;
-    p.part_ml_off = rows * D * sizeof(float);
+    p.part_ml_off = rows * D * sizeof(uint16_t);  // fp16 normalised outputs
     p.bytes = p.part_ml_off + rows * 2 * sizeof(float);
   }
   return p;

@@ -172,7 +172,9 @@ int ddtree_build_batched(const float* logp, const int32_t* token, int L, int K, 
  * out[n,h] = sum_j softmax_j(scale * q[n,h] . k[g,j]) v[g,j] over rows
  * j in [0,S) and j = S + m for every m set in anc[n]; fp32 accumulation and
  * online softmax, bf16 rounding of the softmax weights before the P.V
- * product; output rounded to bf16 (to nearest even).
+ * product; when the key range is split over workgroups, each split's
+ * output is normalised by its own sum and kept in fp16 (2^-11 relative)
+ * until the fp32 merge; output rounded to bf16 (to nearest even).
  * ---------------------------------------------------------------------- */
 int ddtree_tree_attn_workspace_bytes(int N, int Hq, int Hkv, int D, int S,
                                      size_t* bytes /* host */);
