@@ -131,3 +131,23 @@ def test_long_context_sampled():
     nodes = [0, 1, 100, 256]
     heads = [0, 13, 31]
     _run(qkv.q_bits, qkv.q, qkv.kv_bits[0], qkv.kv[0], w.S, tree.anc, nodes=nodes, heads=heads)
+
+
+def test_max_nodes_random_tree_sampled():
+    """The largest tree (N = DDTREE_MAX_B + 1 = 1025 nodes, 33 mask words) of
+    random depth at the budget-sweep shape (Hq = 32, Hkv = 8, D = 128,
+    S = 8192); sampled (node, head) rows, the deepest node included."""
+    N, Hq, Hkv, D, S = 1025, 32, 8, 128, 8192
+    q_bits, q, kv_bits, kv, g = _inputs(N, Hq, Hkv, D, S, 5)
+    anc = _tree_anc("random", N, g)
+    popc = np.array([sum(bin(int(w)).count("1") for w in row) for row in anc.view(np.uint32)])
+    deepest = int(np.argmax(popc))
+    nodes = sorted({0, 1, 511, 1024, deepest})
+    _run(q_bits, q, kv_bits, kv, S, anc, nodes=nodes, heads=[0, 5, 31])
+
+
+def test_max_nodes_d64_full():
+    """1025 nodes at D = 64, G = 4: every output element."""
+    q_bits, q, kv_bits, kv, g = _inputs(1025, 4, 1, 64, 300, 6)
+    anc = _tree_anc("random", 1025, g)
+    _run(q_bits, q, kv_bits, kv, 300, anc)
