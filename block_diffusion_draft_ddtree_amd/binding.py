@@ -298,17 +298,22 @@ def _host_ints(values) -> ctypes.Array:
 
 
 def ddtree_build_batched(logp: torch.Tensor, token: torch.Tensor, B: int,
-                         root_token: torch.Tensor, mask_words: int | None = None, stream=None):
+                         root_token: torch.Tensor, mask_words: int | None = None, out=None,
+                         stream=None):
     """[R, L, K] tables, root_token int32 [R] -> (parent, depth, node_token,
-    score) int32/fp32 [R, B + 1] and anc [R, B + 1, W]."""
+    score) int32/fp32 [R, B + 1] and anc [R, B + 1, W]; `out` may supply
+    those five tensors (then nothing is allocated)."""
     R, L, K = logp.shape
     N = B + 1
     W = (N + 31) // 32 if mask_words is None else mask_words
     dev = logp.device
     i32 = dict(dtype=torch.int32, device=dev)
-    parent, depth, node_token = (torch.empty((R, N), **i32) for _ in range(3))
-    score = torch.empty((R, N), dtype=torch.float32, device=dev)
-    anc = torch.empty((R, N, W), **i32)
+    if out is None:
+        parent, depth, node_token = (torch.empty((R, N), **i32) for _ in range(3))
+        score = torch.empty((R, N), dtype=torch.float32, device=dev)
+        anc = torch.empty((R, N, W), **i32)
+    else:
+        parent, depth, node_token, score, anc = out
     _check(lib().ddtree_build_batched(
         _dev(logp, torch.float32, "logp"), _dev(token, torch.int32, "token"), L, K, B, R,
         _dev(root_token, torch.int32, "root_token"), _dev(parent, torch.int32, "parent"),
@@ -353,14 +358,17 @@ def ddtree_tree_attn_batched(q: torch.Tensor, kv: torch.Tensor, layer: int, S, a
 
 
 def ddtree_accept_walk_batched(parent: torch.Tensor, node_token: torch.Tensor, L: int,
-                               target: torch.Tensor, stream=None):
+                               target: torch.Tensor, out=None, stream=None):
     """[R, N] trees and target tokens -> (acc int32 [R, L + 1], n_acc int32
-    [R], next_bonus int32 [R])."""
+    [R], next_bonus int32 [R]); `out` may supply those three tensors."""
     R, N = parent.shape
     i32 = dict(dtype=torch.int32, device=parent.device)
-    acc = torch.empty((R, L + 1), **i32)
-    n_acc = torch.empty(R, **i32)
-    next_bonus = torch.empty(R, **i32)
+    if out is None:
+        acc = torch.empty((R, L + 1), **i32)
+        n_acc = torch.empty(R, **i32)
+        next_bonus = torch.empty(R, **i32)
+    else:
+        acc, n_acc, next_bonus = out
     _check(lib().ddtree_accept_walk_batched(
         _dev(parent, torch.int32, "parent"), _dev(node_token, torch.int32, "node_token"), N, L, R,
         _dev(target, torch.int32, "target"), _dev(acc, torch.int32, "acc"),

@@ -112,7 +112,8 @@ class DraftTreeRound:
 class BatchedDraftTreeRound:
     """One round for R requests at once: each has its own drafter rows, tree,
     prefix length S[r] and KV cache (kv: [R, layers, 2, Hkv, S_cap, D]); all
-    share L, V, K, B and the attention shape."""
+    share L, V, K, B and the attention shape. Every buffer is allocated here,
+    so a round enqueues only libddtree kernels."""
 
     def __init__(self, shape: RoundShape, S, device="cuda"):
         s = shape
@@ -129,8 +130,14 @@ class BatchedDraftTreeRound:
         self.attn_out = torch.empty((s.layers, R, N, s.Hq, s.D), dtype=torch.bfloat16, device=dev)
         self.ws_attn = bd.workspace(
             bd.ddtree_tree_attn_batched_workspace_bytes(self.S, N, s.Hq, s.Hkv, s.D), dev)
-        self.tree = None
-        self.walk_out = None
+        # parent, depth, node_token, score [R, N]; anc [R, N, W]
+        self.tree = (torch.empty((R, N), **i32), torch.empty((R, N), **i32),
+                     torch.empty((R, N), **i32),
+                     torch.empty((R, N), dtype=torch.float32, device=dev),
+                     torch.empty((R, N, s.W), **i32))
+        # acc [R, L + 1], n_acc [R], next_bonus [R]
+        self.walk_out = (torch.empty((R, s.L + 1), **i32), torch.empty(R, **i32),
+                         torch.empty(R, **i32))
 
     def topk(self, logits):
         """logits fp32 [R * L, V]: request r's block positions at rows r * L ..."""
@@ -138,9 +145,9 @@ class BatchedDraftTreeRound:
 
     def build(self):
         s = self.shape
-        self.tree = bd.ddtree_build_batched(self.logp.view(self.R, s.L, s.K),
-                                            self.token.view(self.R, s.L, s.K), s.B,
-                                            self.root_token, s.W)
+        bd.ddtree_build_batched(self.logp.view(self.R, s.L, s.K),
+                                self.token.view(self.R, s.L, s.K), s.B, self.root_token, s.W,
+                                out=self.tree)
 
     def attn(self, layer: int, q, kv):
         """q bf16 [R, N, Hq, D] for this layer; kv [R, layers, 2, Hkv, S_cap, D]."""
@@ -150,8 +157,8 @@ class BatchedDraftTreeRound:
     def walk(self, target):
         """target int32 [R, N]: the target's token per node of every request."""
         parent, _, node_token, _, _ = self.tree
-        self.walk_out = bd.ddtree_accept_walk_batched(parent, node_token, self.shape.L, target)
-        return self.walk_out
+        return bd.ddtree_accept_walk_batched(parent, node_token, self.shape.L, target,
+                                             out=self.walk_out)
 
     def compact(self, kv):
         acc, n_acc, _ = self.walk_out
