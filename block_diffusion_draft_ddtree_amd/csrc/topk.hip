@@ -500,6 +500,41 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   const uint32_t d0 = ds0.digit;
   const uint32_t need = ds0.need;
   const bool take_bin = need == ds0.in_bin;
+  if (ds0.above + ds0.in_bin <= (uint32_t)kMergeThreads) {
+    // The boundary bucket and everything above it fit one element per
+    // thread: rank them all directly (exact order: logit, then id) and keep
+    // ranks below K, skipping the refinement. Typically K plus the few
+    // dozen values that share the K-th largest's bucket.
+    for (int r = 0; r < per; ++r) {
+      const int i = t + kMergeThreads * r;
+      if (i < n_all) {
+        const float x = elem_x(i);
+        if (rel_digit(M, x) >= d0) {
+          const uint32_t pos = atomicAdd(&s.nwin, 1u);
+          s.wx[pos] = x;
+          s.wi[pos] = elem_i(i);
+        }
+      }
+    }
+    __syncthreads();
+    const int n2 = (int)s.nwin;  // == above + in_bin
+    const int npad = (n2 + 15) & ~15;
+    if (t >= n2 && t < npad) {
+      s.wx[t] = -INFINITY;
+      s.wi[t] = 0x7FFFFFFF;
+    }
+    __syncthreads();
+    if (t < n2) {
+      const float xt = s.wx[t];
+      const int it = s.wi[t];
+      const int rank = rank_among(s.wx, s.wi, npad, xt, it);
+      if (rank < K) {
+        out_lp[rank] = xt - lse;
+        out_tok[rank] = it;
+      }
+    }
+    return;
+  }
   uint32_t tkey = 0u, tik = 0u;
   const uint32_t idx_mask = idx_passes >= 4 ? 0xFFFFFFFFu : ((1u << (8 * idx_passes)) - 1u);
   if (!take_bin) {
