@@ -52,5 +52,31 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+C_DRIVER_SRC = os.path.join(ROOT, "tests", "c", "abi_round.c")
+C_DRIVER = os.path.join(ROOT, "tests", "c", "abi_round")
+
+
+def build_c_driver(verbose: bool = False) -> str:
+    """Compile the plain-C program that runs a round through the C ABI
+    (host code only: gcc against the HIP runtime and libddtree)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [
+        shutil.which("gcc") or "gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__",
+        "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+        C_DRIVER_SRC, "-o", C_DRIVER + ".tmp", "-L", PKG, "-lddtree",
+        "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+        "-Wl,-rpath,$ORIGIN/../../block_diffusion_draft_ddtree_amd",
+        "-Wl,-rpath," + os.path.join(rocm, "lib"),
+    ]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(C_DRIVER + ".tmp", C_DRIVER)
+    return C_DRIVER
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_driver(verbose=True))
