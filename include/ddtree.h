@@ -256,7 +256,9 @@ int ddtree_target_argmax(const void* logits, int dtype, int64_t row_stride, int 
  *   counter = (v >> 2, n, offset mod 2^32, offset >> 32), output word v & 3
  *   u       = ((word >> 9) + 0.5) * 2^-23   (exact in fp32, inside (0, 1))
  * so a result is a pure function of (logits, T, seed, offset): pass a new
- * offset every round. The key is formed in fp32 (in base 2, the same
+ * offset every round. For several requests pass their rows stacked (N is
+ * then the total): row n's draws use counter word n, so every request's
+ * nodes draw independent numbers. The key is formed in fp32 (in base 2, the same
  * argmax); it can pick differently from an exact evaluation only where two
  * tokens' keys are within fp32 rounding of each other.
  *
