@@ -1,0 +1,102 @@
+"""GPU parity over a seeded sweep of shapes: tree attention (single and
+batched calls), top-K and the tree build, each against the oracle.
+
+Every case draws its shape from a fixed seed: node counts across the tile
+and mask-word boundaries, both head sizes, group sizes 1-8, prefixes from
+empty to several splits, slack in the cache capacity, extra mask words,
+random tree shapes; top-K rows of odd lengths and K up to the row; trees
+from tie-rich and deep tables. Bounds as in the per-kernel tests:
+attention |gpu - oracle| <= 2e-2 + 1e-2 |oracle|, integer outputs exact,
+log-probs within 1e-5."""
+import numpy as np
+import pytest
+
+from block_diffusion_draft_ddtree_amd import binding as bd
+from block_diffusion_draft_ddtree_amd import synth
+from oracle import attention as oa
+from oracle import softmax_topk as st
+from oracle import tree as ot
+
+from gpu_helpers import assert_attn_close, down, down_bf16_f32, say, up, up_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _random_parent(g, N):
+    kind = g.integers(0, 3)
+    if kind == 0:
+        return [-1] + list(range(N - 1))                       # chain
+    if kind == 1:
+        return [-1] + [0] * (N - 1)                            # star
+    return [-1] + [int(g.integers(0, n)) for n in range(1, N)]  # random recursive
+
+
+@pytest.mark.parametrize("case", range(64))
+def test_attention_shapes(case):
+    g = synth.rng("test", 800, case)
+    D = int(g.choice([64, 128]))
+    Hkv = int(g.choice([1, 2, 4]))
+    G = int(g.choice([1, 2, 4, 8]))
+    Hq = Hkv * G
+    N = int(g.choice([1, 2, 31, 32, 33, 63, 64, 65, 97, 129, 200]))
+    S = int(g.choice([0, 1, 37, 128, 255, 600, 1500]))
+    S_cap = S + N + int(g.integers(0, 40))
+    W = (N + 31) // 32 + int(g.integers(0, 2))
+    scale = float(g.uniform(0.05, 0.2))
+    say(f"sweep attn case={case} N={N} Hq={Hq} Hkv={Hkv} D={D} S={S} S_cap={S_cap} W={W}")
+    q_bits, q = synth.normal_bf16(g, (N, Hq, D))
+    kv_bits, kv = synth.normal_bf16(g, (2, Hkv, S_cap, D))
+    anc = ot.ancestor_mask(_random_parent(g, N), W)
+    out = bd.ddtree_tree_attn(up_bf16(q_bits), up_bf16(kv_bits[0]), up_bf16(kv_bits[1]), S,
+                              up(anc.view(np.int32)), scale)
+    ref = oa.tree_attention(q, kv[0], kv[1], S, anc, scale)
+    assert_attn_close(down_bf16_f32(out), ref, f"case {case}")
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_batched_attention_shapes(case):
+    g = synth.rng("test", 801, case)
+    R = int(g.integers(2, 7))
+    D = int(g.choice([64, 128]))
+    Hkv = int(g.choice([1, 2, 4]))
+    Hq = Hkv * int(g.choice([1, 4, 8]))
+    N = int(g.choice([1, 17, 33, 65]))
+    S = [int(x) for x in g.choice([0, 5, 100, 513, 1024, 2000], size=R)]
+    layers = 2
+    S_cap = max(S) + N + int(g.integers(0, 9))
+    say(f"sweep batched case={case} R={R} N={N} Hq={Hq} Hkv={Hkv} D={D} S={S}")
+    q_bits, q = synth.normal_bf16(g, (R, N, Hq, D))
+    kv_bits, kv = synth.normal_bf16(g, (R, layers, 2, Hkv, S_cap, D))
+    anc = np.stack([ot.ancestor_mask(_random_parent(g, N)) for _ in range(R)])
+    out = down_bf16_f32(bd.ddtree_tree_attn_batched(up_bf16(q_bits), up_bf16(kv_bits), 1, S,
+                                                    up(anc.view(np.int32))))
+    for r in range(R):
+        ref = oa.tree_attention(q[r], kv[r, 1, 0], kv[r, 1, 1], S[r], anc[r])
+        assert_attn_close(out[r], ref, f"case {case} request {r}")
+
+
+@pytest.mark.parametrize("case", range(32))
+def test_topk_and_build_shapes(case):
+    g = synth.rng("test", 802, case)
+    L = int(g.integers(1, 9))
+    V = int(g.choice([5, 64, 257, 1000, 4097, 9000]))
+    K = int(min(V, g.choice([1, 2, 8, 33, 64, 100])))
+    if g.uniform() < 0.4:
+        x = synth.deep_logits(L, V, g).astype(np.float32)
+    else:
+        x = np.round(g.standard_normal((L, V)) * 3).astype(np.float32)  # tie-rich
+    say(f"sweep topk/build case={case} L={L} V={V} K={K}")
+    lp, tok = bd.ddtree_topk(up(x), K)
+    lp, tok = down(lp), down(tok)
+    lp_ref, tok_ref = st.topk(x, K)
+    np.testing.assert_array_equal(tok, tok_ref)
+    np.testing.assert_allclose(lp, lp_ref, atol=1e-5, rtol=0)
+    total = sum(K ** d for d in range(1, L + 1))
+    B = int(min(total, g.choice([1, 5, 16, 64, 100, 300])))
+    root = int(g.integers(0, V))
+    parent, depth, ntok, score, anc = bd.ddtree_build(up(lp), up(tok), B, up(np.array([root], np.int32)))
+    tree = ot.build_tree(lp, tok, B, root)
+    np.testing.assert_array_equal(down(parent), tree.parent)
+    np.testing.assert_array_equal(down(depth), tree.depth)
+    np.testing.assert_array_equal(down(ntok), tree.token)
+    np.testing.assert_array_equal(down(anc).view(np.uint32), tree.anc)
