@@ -11,8 +11,9 @@
 //   merge kernel  grid L, 1024 threads. Combines the (max, sum) pairs into
 //                 lse, keeps the candidates >= tau = max_c t_c (a valid
 //                 lower bound of the row's K-th largest, so every top-K
-//                 element survives), ranks the survivors exactly in LDS and
-//                 writes logp = x - lse and the token ids in rank order.
+//                 element survives), narrows them to the first-digit bucket
+//                 of the K-th largest and above, ranks those exactly in LDS
+//                 and writes logp = x - lse and the token ids in rank order.
 //
 // Selection is a radix select. Its first digit is relative to the reference
 // maximum m: digit = bits(fl(m - x) + 1) >> 19, clamped (16 bins per octave
@@ -33,6 +34,7 @@ constexpr int kLooseExtra = 256;                     // slots beyond K per chunk
 constexpr int kMergeThreads = 1024;
 constexpr int kSurvCap = 16384;                      // survivors selected in LDS (128 KB)
 constexpr int kLoadBatch = 8;                        // candidates loaded per thread at once
+constexpr int kRankAllMax = 256;                     // survivors ranked all against all
 
 // Larger digit = closer to the reference maximum (monotone in x).
 __device__ __forceinline__ uint32_t rel_digit(float ref_max, float x) {
@@ -342,8 +344,32 @@ struct MergeLds {
   alignas(16) int wi[DDTREE_MAX_K];
   float lse, tau, M;
   int total;
-  uint32_t nsurv, nwin;
+  uint32_t nsurv, nkeep, nwin;
 };
+
+// Rank the n pairs in xs/is (n <= kMergeThreads, arrays padded to a multiple
+// of 16 with room) among themselves, one per thread, and write those ranked
+// below K. Starts with a barrier (after the pairs' writes).
+__device__ __forceinline__ void rank_and_write(float* xs, int* is, int n, int K, float lse,
+                                               float* out_lp, int32_t* out_tok) {
+  const int t = threadIdx.x;
+  const int npad = (n + 15) & ~15;
+  __syncthreads();
+  if (t >= n && t < npad) {
+    xs[t] = -INFINITY;
+    is[t] = 0x7FFFFFFF;
+  }
+  __syncthreads();
+  if (t < n) {
+    const float xt = xs[t];
+    const int it = is[t];
+    const int rank = rank_among(xs, is, npad, xt, it);
+    if (rank < K) {
+      out_lp[rank] = xt - lse;
+      out_tok[rank] = it;
+    }
+  }
+}
 
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     int C, int K, int cap, int idx_passes, const float4* __restrict__ stats,
@@ -393,148 +419,118 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
       s.tau = tau;
       s.lse = M + logf(S);
       s.nsurv = 0u;
+      s.nkeep = 0u;
       s.nwin = 0u;
       s.sh.out_count = 0u;
     }
   }
+  init_hists(s.sh);
   __syncthreads();
   const int total = s.total;
-  const float tau = s.tau;
-
-  // Survivors: candidates >= tau, loaded kLoadBatch per thread at a time.
-  for (int g0 = 0; g0 < total; g0 += kMergeThreads * kLoadBatch) {
-    float xv[kLoadBatch];
-    int iv[kLoadBatch];
-#pragma unroll
-    for (int r = 0; r < kLoadBatch; ++r) {
-      const int i = g0 + t + kMergeThreads * r;
-      xv[r] = -INFINITY;
-      iv[r] = -1;
-      if (i < total) {
-        int lo = 0, hi = C;  // last chunk with offs[c] <= i
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (s.offs[mid] <= i) lo = mid; else hi = mid;
-        }
-        const int64_t at = (int64_t)lo * cap + (i - s.offs[lo]);
-        xv[r] = cx[at];
-        iv[r] = ci[at];
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kLoadBatch; ++r) {
-      const bool keep = iv[r] >= 0 && xv[r] >= tau;
-      const uint64_t bm = ddt::ballot(keep);
-      uint32_t wb = 0u;
-      if (lane == 0 && bm) wb = atomicAdd(&s.nsurv, (uint32_t)__popcll(bm));
-      wb = (uint32_t)__builtin_amdgcn_readfirstlane((int)wb);
-      if (keep) {
-        const uint32_t pos = wb + ddt::lanes_below(bm);
-        if (pos < (uint32_t)kSurvCap) {
-          s.sx[pos] = xv[r];
-          s.si[pos] = iv[r];
-        }
-      }
-    }
-  }
-  __syncthreads();
-  const int nsurv = (int)s.nsurv;
-  const float lse = s.lse;
+  const float tau = s.tau, M = s.M, lse = s.lse;
   float* out_lp = logp + (int64_t)row * K;
   int32_t* out_tok = token + (int64_t)row * K;
 
-  if (nsurv <= kMergeThreads) {
-    // Rank every survivor among the survivors; ranks below K are outputs.
-    const int npad = (nsurv + 15) & ~15;
-    if (t >= nsurv && t < npad) {
-      s.sx[t] = -INFINITY;
-      s.si[t] = 0x7FFFFFFF;
+  // Candidate i of the row (the chunks' lists concatenated): its chunk is
+  // found by binary search over the prefix offsets.
+  auto cand_at = [&](int i) -> int64_t {
+    int lo = 0, hi = C;  // last chunk with offs[c] <= i
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s.offs[mid] <= i) lo = mid; else hi = mid;
     }
-    __syncthreads();
-    if (t < nsurv) {
-      const float xt = s.sx[t];
-      const int it = s.si[t];
-      const int rank = rank_among(s.sx, s.si, npad, xt, it);
-      if (rank < K) {
-        out_lp[rank] = xt - lse;
-        out_tok[rank] = it;
+    return (int64_t)lo * cap + (i - s.offs[lo]);
+  };
+  // One pass over the candidates, kLoadBatch per thread at a time: keep(x)
+  // says which to append to sx/si (one LDS atomic per wave on `counter`;
+  // slots past kSurvCap are dropped, the counter still counts them).
+  auto gather = [&](uint32_t* counter, auto keep) {
+    for (int g0 = 0; g0 < total; g0 += kMergeThreads * kLoadBatch) {
+      float xv[kLoadBatch];
+      int iv[kLoadBatch];
+#pragma unroll
+      for (int r = 0; r < kLoadBatch; ++r) {
+        const int i = g0 + t + kMergeThreads * r;
+        xv[r] = -INFINITY;
+        iv[r] = -1;
+        if (i < total) {
+          const int64_t at = cand_at(i);
+          xv[r] = cx[at];
+          iv[r] = ci[at];
+        }
       }
-    }
-    return;
-  }
-
-  // More survivors than threads: exact radix select of the K largest, over
-  // the survivors in LDS when they fit, else over all candidates in global
-  // memory (only tie-heavy rows get there), then rank the K winners.
-  const bool in_lds = nsurv <= kSurvCap;
-  const int n_all = in_lds ? nsurv : total;
-  const float M = s.M;
-  auto elem_x = [&](int i) -> float {
-    if (in_lds) return s.sx[i];
-    int lo = 0, hi = C;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s.offs[mid] <= i) lo = mid; else hi = mid;
-    }
-    return cx[(int64_t)lo * cap + (i - s.offs[lo])];
-  };
-  auto elem_i = [&](int i) -> int {
-    if (in_lds) return s.si[i];
-    int lo = 0, hi = C;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s.offs[mid] <= i) lo = mid; else hi = mid;
-    }
-    return ci[(int64_t)lo * cap + (i - s.offs[lo])];
-  };
-  const int per = (n_all + kMergeThreads - 1) / kMergeThreads;
-
-  init_hists(s.sh);
-  __syncthreads();
-  for (int r = 0; r < per; ++r) {  // pass 0
-    const int i = t + kMergeThreads * r;
-    if (i < n_all) atomicAdd(&s.sh.hist[0][rel_digit(M, elem_x(i))], 1u);
-  }
-  __syncthreads();
-  const DigitSel ds0 = find_digit(s.sh.hist[0], (uint32_t)K);
-  const uint32_t d0 = ds0.digit;
-  const uint32_t need = ds0.need;
-  const bool take_bin = need == ds0.in_bin;
-  if (ds0.above + ds0.in_bin <= (uint32_t)kMergeThreads) {
-    // The boundary bucket and everything above it fit one element per
-    // thread: rank them all directly (exact order: logit, then id) and keep
-    // ranks below K, skipping the refinement. Typically K plus the few
-    // dozen values that share the K-th largest's bucket.
-    for (int r = 0; r < per; ++r) {
-      const int i = t + kMergeThreads * r;
-      if (i < n_all) {
-        const float x = elem_x(i);
-        if (rel_digit(M, x) >= d0) {
-          const uint32_t pos = atomicAdd(&s.nwin, 1u);
-          s.wx[pos] = x;
-          s.wi[pos] = elem_i(i);
+#pragma unroll
+      for (int r = 0; r < kLoadBatch; ++r) {
+        const bool k = iv[r] >= 0 && keep(xv[r]);
+        const uint64_t bm = ddt::ballot(k);
+        uint32_t wb = 0u;
+        if (lane == 0 && bm) wb = atomicAdd(counter, (uint32_t)__popcll(bm));
+        wb = (uint32_t)__builtin_amdgcn_readfirstlane((int)wb);
+        if (k) {
+          const uint32_t pos = wb + ddt::lanes_below(bm);
+          if (pos < (uint32_t)kSurvCap) {
+            s.sx[pos] = xv[r];
+            s.si[pos] = iv[r];
+          }
         }
       }
     }
-    __syncthreads();
-    const int n2 = (int)s.nwin;  // == above + in_bin
-    const int npad = (n2 + 15) & ~15;
-    if (t >= n2 && t < npad) {
-      s.wx[t] = -INFINITY;
-      s.wi[t] = 0x7FFFFFFF;
-    }
-    __syncthreads();
-    if (t < n2) {
-      const float xt = s.wx[t];
-      const int it = s.wi[t];
-      const int rank = rank_among(s.wx, s.wi, npad, xt, it);
-      if (rank < K) {
-        out_lp[rank] = xt - lse;
-        out_tok[rank] = it;
-      }
-    }
+  };
+
+  // Survivors: the candidates >= tau (every top-K element is one), each also
+  // counted in the histogram of the first digit relative to the row max.
+  gather(&s.nsurv, [&](float x) {
+    const bool k = x >= tau;
+    if (k) atomicAdd(&s.sh.hist[0][rel_digit(M, x)], 1u);
+    return k;
+  });
+  __syncthreads();
+  int nsurv = (int)s.nsurv;
+  if (nsurv <= kRankAllMax) {
+    // Few survivors: rank each among all of them.
+    rank_and_write(s.sx, s.si, nsurv, K, lse, out_lp, out_tok);
     return;
   }
+
+  // The bucket d0 of the row's K-th largest: survivors in it or above it
+  // hold the top K (typically K plus a few dozen values).
+  const DigitSel ds0 = find_digit(s.sh.hist[0], (uint32_t)K);
+  const uint32_t d0 = ds0.digit;
+  const uint32_t n_top = ds0.above + ds0.in_bin;
+  bool in_lds = nsurv <= kSurvCap;
+  if (!in_lds && n_top <= (uint32_t)kSurvCap) {
+    // The survivors overflowed LDS (a large K): gather only bucket d0 and
+    // above, in a second pass.
+    gather(&s.nkeep, [&](float x) { return x >= tau && rel_digit(M, x) >= d0; });
+    __syncthreads();
+    nsurv = (int)n_top;
+    in_lds = true;
+  }
+  if (n_top <= (uint32_t)kMergeThreads) {
+    // Bucket d0 and above fit one per thread (then they are in LDS): move
+    // them to wx/wi and rank them among themselves.
+    for (int i = t; i < nsurv; i += kMergeThreads) {
+      const float x = s.sx[i];
+      if (rel_digit(M, x) >= d0) {
+        const uint32_t pos = atomicAdd(&s.nwin, 1u);
+        s.wx[pos] = x;
+        s.wi[pos] = s.si[i];
+      }
+    }
+    rank_and_write(s.wx, s.wi, (int)n_top, K, lse, out_lp, out_tok);
+    return;
+  }
+
+  // Many values in bucket d0 or above (a large K, or a tie-heavy row): exact
+  // radix select of the K largest inside bucket d0, over the survivors in
+  // LDS, else over the candidates in global memory (those below tau are not
+  // survivors there and are skipped), then rank the K winners.
+  const int n_all = in_lds ? nsurv : total;
+  auto elem_x = [&](int i) -> float { return in_lds ? s.sx[i] : cx[cand_at(i)]; };
+  auto elem_i = [&](int i) -> int { return in_lds ? s.si[i] : ci[cand_at(i)]; };
+  const int per = (n_all + kMergeThreads - 1) / kMergeThreads;
+  const uint32_t need = ds0.need;
+  const bool take_bin = need == ds0.in_bin;
   uint32_t tkey = 0u, tik = 0u;
   const uint32_t idx_mask = idx_passes >= 4 ? 0xFFFFFFFFu : ((1u << (8 * idx_passes)) - 1u);
   if (!take_bin) {
@@ -542,7 +538,9 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
         s.sh, need, per, idx_passes, 1,
         [&](int r) {
           const int i = t + kMergeThreads * r;
-          return i < n_all && rel_digit(M, elem_x(i)) == d0;
+          if (i >= n_all) return false;
+          const float x = elem_x(i);
+          return x >= tau && rel_digit(M, x) == d0;
         },
         [&](int r) { return ddt::f32_key(elem_x(t + kMergeThreads * r)); },
         [&](int r) { return idx_mask - (uint32_t)elem_i(t + kMergeThreads * r); }, tkey, tik);
@@ -551,6 +549,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     const int i = t + kMergeThreads * r;
     if (i >= n_all) continue;
     const float x = elem_x(i);
+    if (!(x >= tau)) continue;
     const uint32_t d = rel_digit(M, x);
     bool sel = d > d0;
     if (d == d0) {
@@ -569,19 +568,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
       }
     }
   }
-  const int kpad = (K + 15) & ~15;
-  if (t >= K && t < kpad) {
-    s.wx[t] = -INFINITY;
-    s.wi[t] = 0x7FFFFFFF;
-  }
-  __syncthreads();
-  if (t < K) {
-    const float xt = s.wx[t];
-    const int it = s.wi[t];
-    const int rank = rank_among(s.wx, s.wi, kpad, xt, it);
-    out_lp[rank] = xt - lse;
-    out_tok[rank] = it;
-  }
+  rank_and_write(s.wx, s.wi, K, K, lse, out_lp, out_tok);
 }
 
 }  // namespace
