@@ -56,6 +56,17 @@ def test_ties_smaller_id_first():
     _check(x, 1024)
 
 
+def test_ties_beyond_lds():
+    """Rows where more than 16 K candidates share the K-th largest's first
+    digit bucket (a constant row; a row whose top level holds 30000 equal
+    values): the merge then selects over the candidates in global memory."""
+    g = synth.rng("test", 504, 0)
+    x = np.zeros((2, 151936), dtype=np.float32)
+    x[1, :] = -1.0
+    x[1, g.choice(151936, 30000, replace=False)] = 2.5
+    _check(x, 1024)
+
+
 def test_signed_zero_and_few_values():
     x = np.zeros((2, 5000), dtype=np.float32)
     x[0, ::3] = -0.0
