@@ -27,8 +27,9 @@
 // and serves the other tiles from its L2.
 //
 // Data movement. K and V blocks go from global memory straight into LDS
-// (global_load_lds, 16 bytes per lane, no registers), double-buffered: the
-// copy of superblock i + 1 is in flight while superblock i is computed. A
+// (buffer loads to LDS, 16 bytes per lane, no registers, bounded by the
+// last key), double-buffered: the copies of superblock i + 1 are in flight
+// while superblock i is computed, one at a time between products. A
 // wave's copy lands 1 KB contiguously (lane l at +16 l), and each lane
 // fetches whichever 16-byte chunk belongs at its slot. K and V rows are
 // row-major with the chunk index XOR-ed by a function of the row (slot =
@@ -164,41 +165,41 @@ __device__ __forceinline__ CopyLanes<D> copy_lanes(int rw, int lane) {
   return cl;
 }
 
-// Copy the 32-key block starting at key0 of K or V into LDS; the two row
-// waves of a stream split the copies. Source = block base (uniform, scalar
-// registers) + the lane's fixed offset. In the last block rows past the
-// last key (KT - 1) are clamped to it: they are real, finite data whose
-// scores are masked and whose weights are exactly 0.
-template <int D, bool IS_V>
-__device__ __forceinline__ void copy_block(const uint16_t* src, int key0, int KT, char* dst_lds,
-                                           int rw, const CopyLanes<D>& cl) {
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle).
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
+// Buffer resource over the 32-key block of K or V starting at key0 (src:
+// the kv-head's row 0), bounded at the last key KT - 1, or empty when the
+// block is not wanted. A copy's lanes past the bound are out of range and
+// write zeros into LDS, so a block reaching past the last key (or lying
+// wholly past it) lands as its real rows followed by zero rows: finite data
+// whose scores are masked and whose weights are exactly 0. The fields are
+// wave-uniform (scalar registers).
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* src, int key0,
+                                                             int KT, bool want) {
   using C = Cfg<D>;
-  const char* base = reinterpret_cast<const char*>(src + (int64_t)key0 * D);
-  const int lane = threadIdx.x & 63;
-  auto off = [&](int i) -> uint32_t {
-    return IS_V ? cl.vb + (uint32_t)(i * C::ROWS_PER_COPY * C::ROWB) : cl.kb[i];
-  };
-  if (key0 + kBK <= KT) {
-#pragma unroll
-    for (int i = 0; i < C::COPIES; ++i) {
-      const int copy = rw * C::COPIES + i;
-      __builtin_amdgcn_global_load_lds(base + off(i), (lds_void_t*)(dst_lds + copy * 1024), 16,
-                                       0, 0);
-    }
-  } else {
-    // Rows clamped to key KT - 1 (the block may lie wholly past it): a
-    // per-lane address from the clamped key, plus the chunk's byte offset
-    // within its row (never negative).
-#pragma unroll
-    for (int i = 0; i < C::COPIES; ++i) {
-      const int copy = rw * C::COPIES + i;
-      const int row = copy_row<D>(rw, i, lane);
-      const int key = min(key0 + row, KT - 1);
-      const char* p = reinterpret_cast<const char*>(src + (int64_t)key * D) +
-                      (off(i) - (uint32_t)(row * C::ROWB));
-      __builtin_amdgcn_global_load_lds(p, (lds_void_t*)(dst_lds + copy * 1024), 16, 0, 0);
-    }
-  }
+  const int rows = want ? max(0, min(kBK, KT - key0)) : 0;
+  const uint64_t a = reinterpret_cast<uint64_t>(rows > 0 ? src + (int64_t)key0 * D : src);
+  // Taken through readfirstlane: the compiler cannot always see that these
+  // are uniform, and a resource in vector registers costs a loop per copy.
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const int nrec = __builtin_amdgcn_readfirstlane(rows * C::ROWB);
+  void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, nrec, kRsrcWord3);
+}
+
+// Copy i of this row wave's share of a K or V block into LDS (the two row
+// waves of a stream split a block's copies): 1 KB, lane l to +16 l, each
+// lane the chunk that belongs at its slot.
+template <int D, bool IS_V>
+__device__ __forceinline__ void copy_part(__amdgpu_buffer_rsrc_t rs, char* dst_lds, int rw,
+                                          const CopyLanes<D>& cl, int i) {
+  using C = Cfg<D>;
+  const uint32_t off = IS_V ? cl.vb + (uint32_t)(i * C::ROWS_PER_COPY * C::ROWB) : cl.kb[i];
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (lds_void_t*)(dst_lds + (rw * C::COPIES + i) * 1024), 16, off, 0, 0, 0);
 }
 
 // Rescaling of the running output is skipped while no query column's
@@ -303,10 +304,12 @@ __device__ __forceinline__ void block_pv(const char* Vb, const VLanes<D>& vl, co
 }
 
 // S^T = K Q^T for this wave's 32 query columns over one 32-key block: one
-// chain of products, with the K operand reads kept a few steps ahead.
-template <int D>
+// chain of products, with the K operand reads kept a few steps ahead and
+// the copies kcopy(0 .. COPIES - 1) (of the next block, into the other
+// stage) placed between the last products.
+template <int D, class KCopy>
 __device__ __forceinline__ f32x16 block_qk(const char* Kb, const bf16x8 (&qf)[Cfg<D>::KS],
-                                           int lane) {
+                                           int lane, KCopy kcopy) {
   using C = Cfg<D>;
   const int j = lane & 31, h = lane >> 5;
   const char* krow = Kb + j * C::ROWB;
@@ -322,14 +325,22 @@ __device__ __forceinline__ f32x16 block_qk(const char* Kb, const bf16x8 (&qf)[Cf
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks)
     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sacc, 0, 0, 0);
-  // Schedule: AHEAD reads, then alternate one product with one read.
+#pragma unroll
+  for (int i = 0; i < C::COPIES; ++i) kcopy(i);
+  // Schedule: AHEAD reads, then alternate one product with one read, then
+  // the last products with the copies between them.
+  static_assert(C::COPIES <= AHEAD, "one copy per trailing product");
   __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
   for (int i = 0; i < C::KS - AHEAD; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < C::COPIES) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
   return sacc;
 }
 
@@ -342,13 +353,15 @@ __device__ __forceinline__ f32x16 block_qk(const char* Kb, const bf16x8 (&qf)[Cf
 // the previous block's products are added, so it also scales that block's
 // pending weights (they were formed against the old reference maximum).
 // For blocks reaching past S, `vis` (block_visibility) masks the scores by
-// a wave-uniform branch that touches only the scores.
-template <int D, bool PV, class Mid>
+// a wave-uniform branch that touches only the scores. The copies
+// vcopy(0 .. COPIES - 1) (this block's V, into the stage the next step
+// reads) go between the products when PV, else after the score reduction.
+template <int D, bool PV, class VCopy>
 __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
                                                  const VLanes<D>& vl, PBlock& pb,
                                                  f32x16 (&o)[Cfg<D>::DT], float& m_run,
                                                  f32x16& lsum, float c, int lane, bool masked,
-                                                 uint32_t vis, Mid mid) {
+                                                 uint32_t vis, VCopy vcopy) {
   using C = Cfg<D>;
   const int h = lane >> 5;
   bf16x8 va[2][C::DT];
@@ -381,10 +394,11 @@ __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
     }
     m_run = m_new;
   }
-  // Work handed in by the caller (copies) goes here, between the score
-  // reduction and the products.
-  __builtin_amdgcn_sched_barrier(0);
-  mid();
+  if (!PV) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < C::COPIES; ++i) vcopy(i);
+  }
   __builtin_amdgcn_sched_barrier(0);
   if (PV) {
     const bf16x8 ones = bf16_ones();
@@ -403,11 +417,16 @@ __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
   for (int r = 0; r < 16; ++r)
     pb.p[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[r], c, neg_m));
   if (PV) {
-    // Interleave: one product, then a slice of the vector work.
+#pragma unroll
+    for (int i = 0; i < C::COPIES; ++i) vcopy(i);
+    // Interleave: one product, then a slice of the vector work, and every
+    // other product a copy.
+    static_assert(2 * C::COPIES <= 2 * C::DT + 2, "a copy every other product");
 #pragma unroll
     for (int i = 0; i < 2 * C::DT + 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
+      if ((i & 1) && (i >> 1) < C::COPIES) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
     }
   }
 }
@@ -468,18 +487,15 @@ __device__ __forceinline__ void attn_workgroup(
   const int soff = st * C::TILEB;
 
   const CopyLanes<D> cl = copy_lanes<D>(rw, lane);
-  // Blocks wholly past the last key are still copied (every row clamped to
-  // the last key) and computed (every key masked): every wave then runs one
-  // straight path, and no stage ever holds data that is not a finite K or V
-  // row.
-  auto copy_k = [&](int sb, char* dst) {
-    copy_block<D, false>(kh, (sb * kStreams + st) * kBK, KT, dst + soff, rw, cl);
-  };
-  auto copy_v = [&](int sb, char* dst) {
-    copy_block<D, true>(vh, (sb * kStreams + st) * kBK, KT, dst + soff, rw, cl);
-  };
+  // Blocks wholly past the last key are still copied (as zero rows) and
+  // computed (every key masked): every wave then runs one straight path,
+  // and no stage ever holds data that is not finite.
   const VLanes<D> vl = v_lanes<D>(lane);
-  copy_k(sb0, k0);
+  {
+    const auto rk = block_rsrc<D>(kh, (sb0 * kStreams + st) * kBK, KT, true);
+#pragma unroll
+    for (int i = 0; i < C::COPIES; ++i) copy_part<D, false>(rk, k0 + soff, rw, cl, i);
+  }
   // Q of the tile goes through LDS too: the 32 rows of row wave rw land in
   // k1 (free until step 0 copies into it) laid out like a K block, copied
   // by that row wave's four stream waves with whole-row coalesced reads
@@ -560,21 +576,25 @@ __device__ __forceinline__ void attn_workgroup(
     const int key0 = (sb * kStreams + st) * kBK;
     // The copies enter the texture-address unit at about 45 B per clock per
     // CU, and a wave whose copies are queued there cannot issue further; so
-    // they are spread over the step: K first, V between the score
-    // reduction and the products.
-    if (sb + 1 < sb1) copy_k(sb + 1, kn);
+    // they are spread over the step one at a time between products: K of
+    // the next superblock (none after the last) in the score products, V
+    // in the P.V products. Branch-free: a block not wanted has an empty
+    // resource.
+    const auto rk = block_rsrc<D>(kh, key0 + kSBK, KT, sb + 1 < sb1);
+    const auto rv = block_rsrc<D>(vh, key0, KT, true);
+    auto kcopy = [&](int i) { copy_part<D, false>(rk, kn + soff, rw, cl, i); };
+    auto vcopy = [&](int i) { copy_part<D, true>(rv, vdst + soff, rw, cl, i); };
     __builtin_amdgcn_sched_barrier(0);
-    const f32x16 sacc = block_qk<D>(kc + soff, qf, lane);
+    const f32x16 sacc = block_qk<D>(kc + soff, qf, lane, kcopy);
     __builtin_amdgcn_sched_barrier(0);
-    auto mid = [&]() { copy_v(sb, vdst); };
     const bool masked = key0 + kBK > S;
     const uint32_t vis = vis_of(key0);
     if (first)
       block_softmax_pv<D, false>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
-                                 masked, vis, mid);
+                                 masked, vis, vcopy);
     else
       block_softmax_pv<D, true>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
-                                masked, vis, mid);
+                                masked, vis, vcopy);
     // Keep the wait for the copies at the end of the step: the scheduler
     // would otherwise hoist it (and the barrier) above the vector work.
     __builtin_amdgcn_sched_barrier(0);
