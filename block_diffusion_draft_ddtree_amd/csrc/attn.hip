@@ -380,7 +380,10 @@ __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
   const bool grow = bmax > m_run + kRescaleSlack;
   if (__builtin_amdgcn_ballot_w64(grow)) {
     const float m_new = fmaxf(m_run, bmax);
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+    // 0 when only m_run is -inf; 1 for a column that has seen no visible key
+    // yet and sees none here either (m_run = m_new = -inf: its output, sum
+    // and pending weights are all still 0), where the difference is NaN.
+    const float corr = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
     for (int r = 0; r < 16; ++r) lsum[r] *= corr;
 #pragma unroll
@@ -482,6 +485,18 @@ __device__ __forceinline__ void attn_workgroup(
   const int NSB = (KT + kSBK - 1) / kSBK;
   const int sb0 = split * sb_per_split;
   const int sb1 = min(NSB, sb0 + sb_per_split);
+  // Superblock order: tile t of a split starts at superblock t mod n of the
+  // split's n and wraps around. The tiles that share a key range sit on one
+  // XCD; in the same order they would all wait on the same lines coming
+  // from HBM at every step, in this order they ask for different
+  // superblocks at first and later find most lines in the XCD's L2. The
+  // online softmax does not depend on the key order.
+  const int nsb = sb1 - sb0;
+  const int rot = tile % nsb;
+  auto sb_at = [&](int i) {
+    const int r = i + rot;
+    return sb0 + (r < nsb ? r : r - nsb);
+  };
   const uint16_t* kh = k + (int64_t)g * S_cap * D;
   const uint16_t* vh = v + (int64_t)g * S_cap * D;
   const int soff = st * C::TILEB;
@@ -492,7 +507,7 @@ __device__ __forceinline__ void attn_workgroup(
   // and no stage ever holds data that is not finite.
   const VLanes<D> vl = v_lanes<D>(lane);
   {
-    const auto rk = block_rsrc<D>(kh, (sb0 * kStreams + st) * kBK, KT, true);
+    const auto rk = block_rsrc<D>(kh, (sb_at(0) * kStreams + st) * kBK, KT, true);
 #pragma unroll
     for (int i = 0; i < C::COPIES; ++i) copy_part<D, false>(rk, k0 + soff, rw, cl, i);
   }
@@ -572,18 +587,18 @@ __device__ __forceinline__ void attn_workgroup(
   // are peeled; the loop is unrolled by two so every access names a fixed
   // array.
   PBlock pb;  // weights of the previous block
-  auto step = [&](int sb, bool first, const char* kc, char* kn, char* vdst, const char* vprev) {
-    const int key0 = (sb * kStreams + st) * kBK;
+  auto step = [&](int i, bool first, const char* kc, char* kn, char* vdst, const char* vprev) {
+    const int key0 = (sb_at(i) * kStreams + st) * kBK;
     // The copies enter the texture-address unit at about 45 B per clock per
     // CU, and a wave whose copies are queued there cannot issue further; so
     // they are spread over the step one at a time between products: K of
     // the next superblock (none after the last) in the score products, V
     // in the P.V products. Branch-free: a block not wanted has an empty
     // resource.
-    const auto rk = block_rsrc<D>(kh, key0 + kSBK, KT, sb + 1 < sb1);
+    const auto rk = block_rsrc<D>(kh, (sb_at(i + 1) * kStreams + st) * kBK, KT, i + 1 < nsb);
     const auto rv = block_rsrc<D>(vh, key0, KT, true);
-    auto kcopy = [&](int i) { copy_part<D, false>(rk, kn + soff, rw, cl, i); };
-    auto vcopy = [&](int i) { copy_part<D, true>(rv, vdst + soff, rw, cl, i); };
+    auto kcopy = [&](int c) { copy_part<D, false>(rk, kn + soff, rw, cl, c); };
+    auto vcopy = [&](int c) { copy_part<D, true>(rv, vdst + soff, rw, cl, c); };
     __builtin_amdgcn_sched_barrier(0);
     const f32x16 sacc = block_qk<D>(kc + soff, qf, lane, kcopy);
     __builtin_amdgcn_sched_barrier(0);
@@ -601,15 +616,15 @@ __device__ __forceinline__ void attn_workgroup(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  step(sb0, true, k0, k1, v0, v1);
+  step(0, true, k0, k1, v0, v1);
 #pragma unroll 1
-  for (int sb = sb0 + 1; sb < sb1; sb += 2) {
-    step(sb, false, k1, k0, v1, v0);
-    if (sb + 1 < sb1) step(sb + 1, false, k0, k1, v0, v1);
+  for (int i = 1; i < nsb; i += 2) {
+    step(i, false, k1, k0, v1, v0);
+    if (i + 1 < nsb) step(i + 1, false, k0, k1, v0, v1);
   }
   // The last block's P.V: its V went to v0 if the last step was an even
   // number of steps after the first, else to v1.
-  block_pv<D>(((sb1 - 1 - sb0) & 1 ? v1 : v0) + soff, vl, pb, o, lsum);
+  block_pv<D>(((nsb - 1) & 1 ? v1 : v0) + soff, vl, pb, o, lsum);
   __syncthreads();
 
   // Merge the four streams. Every wave parks its (reference max, sum) and

@@ -49,9 +49,10 @@ LOGP_ATOL = 1e-5
 
 
 def assert_attn_close(got: np.ndarray, ref: np.ndarray, what: str = "") -> dict:
+    assert np.isfinite(ref).all(), f"{what}: the oracle produced non-finite values"
     err = np.abs(got.astype(np.float64) - ref)
     bound = ATTN_ATOL + ATTN_RTOL * np.abs(ref)
-    bad = err > bound
+    bad = ~(err <= bound)  # NaN outputs count as outside
     stats = {
         "max_abs": float(err.max()),
         "max_rel_to_max": float(err.max() / max(np.abs(ref).max(), 1e-30)),

@@ -70,6 +70,9 @@ def test_tiny_workload():
 @pytest.mark.parametrize("N,Hq,Hkv,D,S,kind", [
     (1, 4, 2, 64, 128, "chain"),      # decode: one node
     (17, 4, 2, 64, 0, "random"),      # no prefix at all
+    (129, 4, 4, 128, 0, "random"),    # no prefix, G = 1: blocks where only some columns see keys
+    (65, 32, 4, 128, 0, "random"),    # no prefix at the 30B head layout
+    (257, 32, 8, 128, 0, "random"),
     (33, 8, 2, 128, 100, "random"),   # ragged prefix (not a multiple of 64)
     (65, 8, 1, 128, 64, "chain"),
     (65, 16, 4, 64, 37, "star"),
