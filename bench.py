@@ -7,7 +7,12 @@ the Qwen3-Coder-30B-A3B verifier shape (32 q-heads / 4 kv-heads, head dim
 128, 48 layers, prefix 4096) with drafter logits [16, 151936] and budget
 B = 64. Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--graph]
+The round is timed as three HIP graph replays per step (top-K and build;
+the attention of every layer; walk and compaction), with events between
+them timing the attention; --eager launches every kernel instead. The
+same steps are also timed with eager launches (eager_us_per_step).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
     python bench.py --copy-probe     # plain device copy of known size (for
                                      # scaling the HBM byte counters)
 
@@ -84,7 +89,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="coder30b_b64")
-    ap.add_argument("--graph", action="store_true", help="replay the round as a HIP graph")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the round as HIP graphs (the default)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel of the timed round instead of replaying graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=30)
     ap.add_argument("--copy-probe", action="store_true",
@@ -184,36 +192,57 @@ def main():
         rnd.walk(tgt)
         rnd.compact(kv, w.S)
 
-    graph = None
-    if args.graph:
+    # The same round as three graphs, so that events recorded between the
+    # replays time the attention of the timed steps.
+    parts = (lambda: (rnd.topk(logits), rnd.build()),
+             lambda: [rnd.attn(layer, q, kv, w.S) for layer in range(w.layers)],
+             lambda: (rnd.walk(tgt), rnd.compact(kv, w.S)))
+    graphs = None
+    if not args.eager:
         for _ in range(2):
             step()
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
+        graphs = []
+        for part in parts:
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                part()
+            graphs.append(gph)
         torch.cuda.synchronize()
 
+    def graph_step(attn_ev=None):
+        graphs[0].replay()
+        if attn_ev is not None:
+            attn_ev[0].record(stream)
+        graphs[1].replay()
+        if attn_ev is not None:
+            attn_ev[1].record(stream)
+        graphs[2].replay()
+
+    def timed_steps(run):
+        """Device and wall time per step over args.steps steps, and the
+        attention's mean time per layer from the events around it."""
+        pairs = [(ev(), ev()) for _ in range(args.steps)]
+        e0, e1 = ev(), ev()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(args.steps):
+            run(pairs[i])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        attn = float(np.mean([a.elapsed_time(b) * 1e3 / w.layers for a, b in pairs]))
+        return e0.elapsed_time(e1) * 1e3 / args.steps, (t1 - t0) * 1e6 / args.steps, attn
+
+    run_step = graph_step if graphs is not None else step
     for _ in range(args.warmup):
-        graph.replay() if graph is not None else step()
+        run_step()
     torch.cuda.synchronize()
 
     # ---- timed region -------------------------------------------------------
-    attn_pairs = [(ev(), ev()) for _ in range(args.steps)]
-    e0, e1 = ev(), ev()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            step(attn_pairs[i])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_us = (t1 - t0) * 1e6 / args.steps
-    gpu_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    gpu_us, wall_us, attn_us = timed_steps(run_step)
+    eager_us = gpu_us if graphs is None else timed_steps(step)[0]
 
     # ---- per-stage device time (HIP events on the launch stream) ----------
     R = args.stage_reps
@@ -243,11 +272,6 @@ def main():
     stage["target_sample"] = timed(lambda i=0: rnd.target_sample(tlog, 1.0, 2024, i), R)
     stage["budget_select"] = timed(lambda i=0: rnd.select_budget(BUDGET_T0, BUDGET_T1), R)
     budget_choice = int(rnd.budget.cpu()[0])
-    if graph is None:
-        attn_live = [a.elapsed_time(b) * 1e3 / w.layers for a, b in attn_pairs]
-        attn_us = float(np.mean(attn_live))
-    else:
-        attn_us = stage["tree_attn"]
     torch.cuda.synchronize()
     a_acc = int(rnd.n_acc.cpu()[0])
     depth = rnd.depth.cpu().numpy()
@@ -283,7 +307,8 @@ def main():
         "data": "synthetic (seeded numpy generators; no weights or datasets)",
         "config": {"workload": w.name, "L": w.L, "V": w.V, "K": w.K, "B": w.B, "Hq": w.Hq,
                    "Hkv": w.Hkv, "D": w.D, "S": w.S, "layers": w.layers,
-                   "mode": "hip-graph" if graph is not None else "eager"},
+                   "mode": "hip-graph" if graphs is not None else "eager"},
+        "eager_us_per_step": round(eager_us, 2),
         "tree_attn_us": round(attn_us, 3),
         "tree_attn_TBps": round(hbm_gbs / 1e3, 3),
         "tree_attn_hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
