@@ -326,7 +326,8 @@ def main():
     }
 
     if args.batch_requests > 0:
-        result["batched"] = batched_leg(w, args.batch_requests, args.steps, args.warmup)
+        result["batched"] = batched_leg(w, args.batch_requests, args.steps, args.warmup,
+                                        use_graphs=not args.eager)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, lg, depth, tgt_np)
     print(json.dumps(result), flush=True)
@@ -337,11 +338,13 @@ def main():
 BATCH_S = [4096, 1024, 3072, 2048, 4096, 512, 3584, 2560]
 
 
-def batched_leg(w, R: int, steps: int, warmup: int):
+def batched_leg(w, R: int, steps: int, warmup: int, use_graphs: bool = True):
     """R requests of workload w in one batched round (own drafter rows,
     tree, prefix length and KV cache each): topk over the stacked rows,
     build, every layer's attention, walk, compaction. Inputs are drawn on
-    the device from a seeded generator."""
+    the device from a seeded generator. Timed like the main round: three
+    graph replays per step with events around the attention, or eager
+    launches."""
     import torch
 
     from block_diffusion_draft_ddtree_amd.round import BatchedDraftTreeRound, RoundShape
@@ -373,15 +376,39 @@ def batched_leg(w, R: int, steps: int, warmup: int):
         rnd.walk(target)
         rnd.compact(kv)
 
+    run_step = step
+    if use_graphs:
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        graphs = []
+        for part in (lambda: (rnd.topk(logits), rnd.build()),
+                     lambda: [rnd.attn(layer, q[layer], kv) for layer in range(w.layers)],
+                     lambda: (rnd.walk(target), rnd.compact(kv))):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                part()
+            graphs.append(gph)
+        torch.cuda.synchronize()
+
+        def run_step(attn_ev=None):
+            graphs[0].replay()
+            if attn_ev is not None:
+                attn_ev[0].record(stream)
+            graphs[1].replay()
+            if attn_ev is not None:
+                attn_ev[1].record(stream)
+            graphs[2].replay()
+
     for _ in range(warmup):
-        step()
+        run_step()
     torch.cuda.synchronize()
     ev = lambda: torch.cuda.Event(enable_timing=True)
     pairs = [(ev(), ev()) for _ in range(steps)]
     e0, e1 = ev(), ev()
     e0.record(stream)
     for i in range(steps):
-        step(pairs[i])
+        run_step(pairs[i])
     e1.record(stream)
     torch.cuda.synchronize()
     round_us = e0.elapsed_time(e1) * 1e3 / steps
@@ -392,7 +419,8 @@ def batched_leg(w, R: int, steps: int, warmup: int):
     nbytes = sum(4 * w.Hkv * (s + w.N) * w.D + 4 * w.N * w.Hq * w.D + 4 * w.N * W for s in S)
     depth = rnd.tree[1].cpu().numpy()
     flops = sum(4 * w.N * w.Hq * w.D * s for s in S) + 4 * w.Hq * w.D * int((depth + 1).sum())
-    return {"R": R, "S": S, "round_us": round(round_us, 2),
+    return {"R": R, "S": S, "mode": "hip-graph" if use_graphs else "eager",
+            "round_us": round(round_us, 2),
             "us_per_request": round(round_us / R, 2),
             "tree_attn_us": round(attn_us, 3),
             "tree_attn_TBps": round(nbytes / (attn_us * 1e-6) / 1e12, 3),
