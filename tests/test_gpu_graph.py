@@ -86,7 +86,7 @@ def test_graph_replays_equal_eager_round():
 
 
 def test_two_rounds_chain_on_device():
-    """Round 2's root is round 1's next bonus, copied on the device; its
+    """The second decoding round's root is the first one's next bonus, copied on the device; its
     prefix grows by the accepted path plus the bonus row. Both rounds are
     checked against the oracle (top-K, tree, walk, compaction)."""
     w, dev, shape, logits, q, kv0, tgt = _setup(layers=1)
