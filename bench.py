@@ -99,6 +99,10 @@ def parse():
                     help="run only the plain copy used to scale the byte counters")
     ap.add_argument("--batch-requests", type=int, default=8,
                     help="requests in the batched-round leg (0 skips it)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workload shapes (8B, 30B at B = 256, long context)")
+    ap.add_argument("--sweep-rounds", type=int, default=1000,
+                    help="decode rounds per budget in the budget-sweep leg (0 skips it)")
     return ap.parse_args()
 
 
@@ -111,6 +115,19 @@ def attn_work(w, depth: np.ndarray):
               + 4 * w.N * W)                 # ancestor mask
     flops = 4 * w.N * w.Hq * w.D * w.S + 4 * w.Hq * w.D * int((depth + 1).sum())
     return nbytes, flops
+
+
+def attn_fracs(nbytes: int, flops: int, us: float) -> dict:
+    """Achieved rates of one attention launch and its fractions of the HBM
+    and MFMA rooflines; `binding_frac` is the larger floor over the time."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
+    t_mfma = flops / (MFMA_BF16_PEAK_TFS * 1e12) * 1e6
+    return {"tree_attn_us": round(us, 3),
+            "TBps": round(nbytes / (us * 1e-6) / 1e12, 3),
+            "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+            "hbm_frac": round(t_hbm / us, 4), "mfma_frac": round(t_mfma / us, 4),
+            "bound": "mfma" if t_mfma > t_hbm else "hbm",
+            "binding_frac": round(max(t_hbm, t_mfma) / us, 4)}
 
 
 def topk_bytes(w):
@@ -328,9 +345,193 @@ def main():
     if args.batch_requests > 0:
         result["batched"] = batched_leg(w, args.batch_requests, args.steps, args.warmup,
                                         use_graphs=not args.eager)
+    # Free the headline round's buffers before the other shapes allocate theirs.
+    del rnd, q, kv, logits, graphs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        result["configs"] = config_legs(args.steps, args.warmup)
+    if args.sweep_rounds > 0:
+        result["budget_sweep"] = sweep_leg(args.sweep_rounds)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, lg, depth, tgt_np)
     print(json.dumps(result), flush=True)
+
+
+def round_leg(w, steps: int, warmup: int, seed: int):
+    """One workload's full round (top-K, build, every layer's attention, walk,
+    compaction) replayed as three HIP graphs per step, with events around the
+    attention: round time, attention time per layer and its roofline
+    fractions. Q/K/V are drawn on the device (seeded torch generator); the
+    walk follows the drafter's peak with p = 0.8 per depth."""
+    import torch
+
+    from block_diffusion_draft_ddtree_amd import synth
+    from block_diffusion_draft_ddtree_amd.round import DraftTreeRound, RoundShape
+
+    dev = torch.device("cuda:0")
+    S_cap = w.S + w.N
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    lg = synth.drafter_logits(w, 0)
+    logits = torch.from_numpy(lg.x).to(dev)
+    q = torch.randn((w.layers, w.N, w.Hq, w.D), generator=gen, device=dev).to(torch.bfloat16)
+    kv = torch.empty((w.layers, 2, w.Hkv, S_cap, w.D), dtype=torch.bfloat16, device=dev)
+    for layer in range(w.layers):
+        kv[layer].copy_(torch.randn(kv[layer].shape, generator=gen, device=dev))
+    shape = RoundShape(w.L, w.V, w.K, w.B, w.Hq, w.Hkv, w.D, w.layers, S_cap)
+    rnd = DraftTreeRound(shape, w.S, dev)
+    rnd.topk(logits)
+    rnd.build()
+    torch.cuda.synchronize()
+    depth = rnd.depth.cpu().numpy()
+    tgt = torch.from_numpy(synth.target_argmax_follow_peak(
+        depth, lg.peak, w.L, w.V, synth.rng(w.family, 0, synth.STREAM_TARGET))).to(dev)
+    parts = (lambda: (rnd.topk(logits), rnd.build()),
+             lambda: [rnd.attn(layer, q, kv, w.S) for layer in range(w.layers)],
+             lambda: (rnd.walk(tgt), rnd.compact(kv, w.S)))
+    for _ in range(2):
+        for part in parts:
+            part()
+    torch.cuda.synchronize()
+    graphs = []
+    for part in parts:
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            part()
+        graphs.append(gph)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        for gph in graphs:
+            gph.replay()
+    pairs = [(ev(), ev()) for _ in range(steps)]
+    e0, e1 = ev(), ev()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for a, b in pairs:
+        graphs[0].replay()
+        a.record(stream)
+        graphs[1].replay()
+        b.record(stream)
+        graphs[2].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    round_us = e0.elapsed_time(e1) * 1e3 / steps
+    attn_us = float(np.mean([a.elapsed_time(b) * 1e3 / w.layers for a, b in pairs]))
+    nbytes, flops = attn_work(w, depth)
+    out = {"S": w.S, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "layers": w.layers,
+           "round_us": round(round_us, 2)}
+    out.update(attn_fracs(nbytes, flops, attn_us))
+    out["algorithmic_bytes"], out["algorithmic_flops"] = nbytes, flops
+    del rnd, q, kv, graphs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def config_legs(steps: int, warmup: int) -> dict:
+    """The other workload shapes, each as a full round: the Qwen3-8B verifier
+    at its prefix 2048 and at 4096 (the HBM-bound case of B = 64 at a 4k
+    context), the 30B verifier at B = 256, and the long-context shape (one
+    layer timed; its attention reported times 48 layers)."""
+    from dataclasses import replace
+
+    from block_diffusion_draft_ddtree_amd import synth
+
+    legs = {}
+    legs["qwen3_8b_s2048"] = round_leg(synth.QWEN3_8B, steps, warmup, 31)
+    legs["qwen3_8b_s4096"] = round_leg(replace(synth.QWEN3_8B, name="qwen3_8b_s4096", S=4096),
+                                       steps, warmup, 32)
+    legs["coder30b_b256"] = round_leg(synth.CODER30B_B256, steps, warmup, 33)
+    lc = round_leg(synth.LONGCTX, steps, warmup, 34)
+    lc["reported_layers"] = synth.LONGCTX_REPORTED_LAYERS
+    lc["attn_us_x_layers"] = round(lc["tree_attn_us"] * synth.LONGCTX_REPORTED_LAYERS, 1)
+    legs["longctx"] = lc
+    return legs
+
+
+def sweep_leg(rounds: int) -> dict:
+    """The budget sweep: for B in 16 ... 512 (K = B, flat logits with weak
+    peaks, 32q/8kv heads, 36 layers, prefix from 8192), `rounds` decode
+    rounds each: top-K, build, attention of all 36 layers at the current
+    prefix length, walk, and compaction of a drawn accepted path (a ~ U[1, L]
+    per round); the prefix then grows by 1 + a. One attention workspace per
+    budget, sized once at the last round's prefix length. Launched eagerly
+    (S changes every round) in chunks held behind a spin kernel, so events
+    see device time, not Python's launch rate."""
+    import torch
+
+    from block_diffusion_draft_ddtree_amd import binding as bd
+    from block_diffusion_draft_ddtree_amd import synth
+    from block_diffusion_draft_ddtree_amd.round import DraftTreeRound, RoundShape
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    chunk = 25
+    out = {"rounds": rounds, "layers": 36, "Hq": 32, "Hkv": 8, "S0": 8192, "per_budget": {}}
+    for B in synth.SWEEP_BUDGETS:
+        w = synth.sweep(B)
+        acc_np, a_np = synth.sweep_accepts(B, w.L, rounds)
+        S_r = synth.sweep_prefix_lengths(w.S, a_np)
+        S_cap = int(S_r[-1]) + w.N
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(5000 + B)
+        logits = [torch.from_numpy(synth.drafter_logits(w, i).x).to(dev) for i in range(2)]
+        q = torch.randn((w.layers, w.N, w.Hq, w.D), generator=gen, device=dev).to(torch.bfloat16)
+        kv = torch.empty((w.layers, 2, w.Hkv, S_cap, w.D), dtype=torch.bfloat16, device=dev)
+        for layer in range(w.layers):
+            kv[layer].copy_(torch.randn(kv[layer].shape, generator=gen, device=dev))
+        acc = torch.from_numpy(acc_np).to(dev)
+        n_acc = torch.from_numpy(a_np).to(dev)
+        tgt = torch.randint(0, w.V, (w.N,), generator=gen, device=dev, dtype=torch.int32)
+        shape = RoundShape(w.L, w.V, w.K, w.B, w.Hq, w.Hkv, w.D, w.layers, S_cap)
+        rnd = DraftTreeRound(shape, int(S_r[-1]), dev)
+        ws_bytes = int(rnd.ws_attn.numel())
+
+        def one_round(r, attn_ev=None):
+            S = int(S_r[r])
+            rnd.topk(logits[r % 2])
+            rnd.build()
+            if attn_ev is not None:
+                attn_ev[0].record(stream)
+            for layer in range(w.layers):
+                rnd.attn(layer, q, kv, S)
+            if attn_ev is not None:
+                attn_ev[1].record(stream)
+            rnd.walk(tgt)
+            bd.ddtree_kv_compact(kv, S, w.N, w.L, acc[r], n_acc[r:r + 1])
+
+        one_round(0)
+        torch.cuda.synchronize()
+        round_ms, attn_ms = 0.0, []
+        for c0 in range(0, rounds, chunk):
+            c1 = min(rounds, c0 + chunk)
+            pairs = [(ev(), ev()) for _ in range(c1 - c0)]
+            e0, e1 = ev(), ev()
+            torch.cuda._sleep(SPIN_CYCLES * 4)
+            e0.record(stream)
+            for r in range(c0, c1):
+                one_round(r, pairs[r - c0])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            round_ms += e0.elapsed_time(e1)
+            attn_ms += [a.elapsed_time(b) / w.layers for a, b in pairs]
+        depth = rnd.depth.cpu().numpy()
+        S_mean = int(np.mean(S_r))
+        from dataclasses import replace
+        nbytes, flops = attn_work(replace(w, S=S_mean), depth)
+        rec = {"S_first": int(S_r[0]), "S_last": int(S_r[-1]), "accepted_mean": float(a_np.mean()),
+               "round_us": round(round_ms * 1e3 / rounds, 2), "attn_workspace_bytes": ws_bytes,
+               "depth_hist": np.bincount(depth).tolist()}
+        rec.update(attn_fracs(nbytes, flops, float(np.mean(attn_ms)) * 1e3))
+        rec["fracs_at_S"] = S_mean
+        out["per_budget"][f"B{B}"] = rec
+        del rnd, q, kv, logits, acc, n_acc
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 # Prefix lengths of the batched leg: R requests of the same model shape with
@@ -428,19 +629,42 @@ def batched_leg(w, R: int, steps: int, warmup: int, use_graphs: bool = True):
             "data": "synthetic (seeded torch device generator)"}
 
 
-def cpu_baseline(w, lg, depth, tgt_np):
-    """The CPU oracle on one whole round (about 10-20 s of host work): top-K,
-    build, every layer's attention (each layer with its own seeded inputs,
-    drawn outside the timed calls), walk, every layer's compaction."""
+def host_info() -> dict:
+    """The host the oracle runs on: CPUs visible to the process, its model,
+    and the numpy/BLAS build and threads."""
+    import platform
+
     from threadpoolctl import threadpool_info
 
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {"cpu_model": model or platform.processor(),
+            "os_cpu_count": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__,
+            "blas": ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in blas),
+            "blas_threads": max([p.get("num_threads", 1) for p in blas] + [1]),
+            "python": platform.python_version()}
+
+
+def oracle_round(w, lg, tgt_np, layers: int) -> dict:
+    """Seconds the CPU oracle spends on each stage of one round of workload
+    w, with `layers` of its attention layers (each with its own seeded
+    inputs, drawn outside the timed calls)."""
     from block_diffusion_draft_ddtree_amd import synth
     from oracle import attention as oa
     from oracle import commit as oc
     from oracle import softmax_topk as st
     from oracle import tree as ot
 
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     t = {"topk": 0.0, "build": 0.0, "attn": 0.0, "walk": 0.0, "compact": 0.0}
     t0 = time.perf_counter()
     lp, tok = st.topk(lg.x, w.K)
@@ -449,7 +673,7 @@ def cpu_baseline(w, lg, depth, tgt_np):
     tree = ot.build_tree(lp.astype(np.float32), tok, w.B, 0)
     t["build"] = time.perf_counter() - t0
     kv_layers = []
-    for layer in range(w.layers):
+    for layer in range(layers):
         qkv = synth.attention_inputs(w, layers=1, round_idx=layer)
         t0 = time.perf_counter()
         oa.tree_attention(qkv.q, qkv.kv[0, 0], qkv.kv[0, 1], w.S, tree.anc)
@@ -463,12 +687,39 @@ def cpu_baseline(w, lg, depth, tgt_np):
         t0 = time.perf_counter()
         oc.kv_compact(kvb, w.S, acc, a)
         t["compact"] += time.perf_counter() - t0
+    return t
+
+
+def cpu_baseline(w, lg, depth, tgt_np):
+    """The CPU oracle on one whole round of the headline workload (all 48
+    layers, not scaled) with numpy's BLAS at its default thread count
+    (`cores` = the BLAS threads it used); and the same oracle pinned to one
+    thread on a bounded sample (top-K, build, walk, 4 attention layers and
+    their compaction), its attention and compaction scaled to all layers."""
+    from threadpoolctl import threadpool_limits
+
+    info = host_info()
+    t = oracle_round(w, lg, tgt_np, w.layers)
     us = 1e6 * sum(t.values())
-    return {"value": round(us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+    sample_layers = 4
+    with threadpool_limits(limits=1):
+        t1 = oracle_round(w, lg, tgt_np, sample_layers)
+    scale = w.layers / sample_layers
+    us1 = 1e6 * (t1["topk"] + t1["build"] + t1["walk"] + scale * (t1["attn"] + t1["compact"]))
+    return {"value": round(us, 1), "unit": "us/step", "cores": info["blas_threads"],
+            "kind": "oracle",
             "sample": (f"one whole round of {w.name}: top-K over all {w.L} rows, tree build, "
                        f"attention of all {w.layers} layers, walk, compaction of all "
-                       f"{w.layers} layers; not scaled"),
-            "stage_s": {k: round(v, 4) for k, v in t.items()}}
+                       f"{w.layers} layers; not scaled; numpy with {info['blas_threads']} "
+                       f"BLAS threads"),
+            "stage_s": {k: round(v, 4) for k, v in t.items()},
+            "single_thread": {"value": round(us1, 1), "unit": "us/step", "cores": 1,
+                              "sample": (f"top-K, build and walk of one round plus "
+                                         f"{sample_layers} of its {w.layers} attention layers "
+                                         f"and their compaction, those two scaled by "
+                                         f"{scale:g}"),
+                              "stage_s": {k: round(v, 4) for k, v in t1.items()}},
+            "host": info}
 
 
 if __name__ == "__main__":

@@ -117,7 +117,7 @@ DDT_API int ddtree_tree_attn_workspace_bytes(int N, int Hq, int Hkv, int D, int 
   if (!bytes) return DDTREE_ERR_INVALID_ARGUMENT;
   const int st = attn_check(N, Hq, Hkv, D, S);
   if (st) return st;
-  *bytes = ddt_host::attn_plan(1, &S, N, Hq, Hkv, D).bytes;
+  *bytes = ddt_host::attn_workspace_bound(1, &S, N, Hq, Hkv, D);
   return DDTREE_OK;
 }
 
@@ -163,7 +163,7 @@ DDT_API int ddtree_tree_attn_batched_workspace_bytes(int R, const int32_t* S, in
   if (!bytes) return DDTREE_ERR_INVALID_ARGUMENT;
   const int st = attn_batch_check(R, S, N, Hq, Hkv, D);
   if (st) return st;
-  *bytes = ddt_host::attn_plan(R, S, N, Hq, Hkv, D).bytes;
+  *bytes = ddt_host::attn_workspace_bound(R, S, N, Hq, Hkv, D);
   return DDTREE_OK;
 }
 

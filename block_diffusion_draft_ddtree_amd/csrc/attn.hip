@@ -856,24 +856,20 @@ __global__ __launch_bounds__(256) void tree_attn_batched_combine_kernel(
                   out + (int64_t)req * N * Hq * D);
 }
 
-// Workgroups resident at once: one per CU. DDTREE_ATTN_SLOTS overrides it
-// (for sweeps).
-int attn_slots() {
-  static const int t = [] {
-    const char* s = std::getenv("DDTREE_ATTN_SLOTS");
-    const int v = s ? std::atoi(s) : 0;
-    return v > 0 ? v : 256;
-  }();
-  return t;
-}
+// Workgroups resident at once: one per CU (LDS holds one).
+constexpr int kSlots = 256;
 
-// DDTREE_ATTN_SBPS, when set, fixes the superblocks per split (for sweeps).
-int attn_sbps_override() {
-  static const int t = [] {
-    const char* s = std::getenv("DDTREE_ATTN_SBPS");
-    return s ? std::atoi(s) : 0;
-  }();
-  return t;
+// Superblocks of a key range of S + N keys.
+inline int n_superblocks(int S, int N) { return (S + N + kSBK - 1) / kSBK; }
+
+// Most splits a request with nsb superblocks may be cut into, when each
+// split covers `per_split` workgroups: enough for four waves of workgroups
+// over the chip, or one split per 16 superblocks when that is more, never
+// more than one per superblock. Non-decreasing in nsb, so a workspace sized
+// for a prefix length serves every shorter one.
+inline int split_budget(int nsb, int per_split) {
+  const int waves4 = (4 * kSlots + per_split - 1) / per_split;
+  return std::min(nsb, std::max(waves4, (nsb + 15) / 16));
 }
 
 // Launch model constants, measured on the 30B verifier shape: one
@@ -890,8 +886,8 @@ constexpr double kStepUs = 1.4, kWgUs = 4.0, kPartBytesPerUs = 5.0e6, kCombineUs
 // least `cap`) once the bound exceeds cap.
 double model_us(int nreq, const int* S, int N, int Hkv, int D, int tiles, int rows_pad, int sbps,
                 double cap) {
-  const int slots = attn_slots();
-  const int cus = std::max(1, slots / kXcds);
+  const int slots = kSlots;
+  const int cus = slots / kXcds;
   int64_t splits_total = 0;
   double work = 0.0, longest = 0.0;
   for (int r = 0; r < nreq; ++r) {
@@ -939,15 +935,16 @@ double model_us(int nreq, const int* S, int N, int Hkv, int D, int tiles, int ro
 }
 
 struct PlanKey {
-  int nreq, N, Hq, Hkv, D, slots;
+  int nreq, N, Hq, Hkv, D;
   int S[DDTREE_MAX_REQ];
 };
 
 // Superblocks per split with the smallest modelled time; ties keep the
 // longer splits. Candidates: every count up to 64 superblocks, beyond that
-// the counts that cut the longest request into 1..64 equal splits. The
-// last choice is kept per thread, so the calls of one round (every layer,
-// same prefix lengths) plan once.
+// the counts that cut the longest request into 1..64 equal splits, keeping
+// only those that cut no request into more splits than its split_budget.
+// The last choice is kept per thread, so the calls of one round (every
+// layer, same prefix lengths) plan once.
 int choose_sbps(int nreq, const int* S, int N, int Hq, int Hkv, int D, int tiles, int rows_pad) {
   thread_local PlanKey last{};
   thread_local int last_sbps = 0;
@@ -957,14 +954,22 @@ int choose_sbps(int nreq, const int* S, int N, int Hq, int Hkv, int D, int tiles
   key.Hq = Hq;
   key.Hkv = Hkv;
   key.D = D;
-  key.slots = attn_slots();
   for (int r = 0; r < nreq; ++r) key.S[r] = S[r];
   if (last_sbps > 0 && std::memcmp(&key, &last, sizeof(PlanKey)) == 0) return last_sbps;
   int nsb_max = 1;
   for (int r = 0; r < nreq; ++r) nsb_max = std::max(nsb_max, (S[r] + N + kSBK - 1) / kSBK);
+  // Shortest split length that keeps every request within its budget.
+  int sbps_min = 1;
+  for (int r = 0; r < nreq; ++r) {
+    const int nsb = n_superblocks(S[r], N);
+    const int b = split_budget(nsb, Hkv * tiles);
+    sbps_min = std::max(sbps_min, (nsb + b - 1) / b);
+  }
   std::vector<int> cand;
   for (int c = 1; c <= std::min(nsb_max, 64); ++c) cand.push_back(c);
   for (int k = 1; k <= 64; ++k) cand.push_back((nsb_max + k - 1) / k);
+  cand.push_back(sbps_min);
+  for (int& c : cand) c = std::max(c, sbps_min);
   std::sort(cand.begin(), cand.end(), std::greater<int>());
   cand.erase(std::unique(cand.begin(), cand.end()), cand.end());
   int best = cand.front();
@@ -995,11 +1000,7 @@ AttnPlan attn_plan(int nreq, const int* S, int N, int Hq, int Hkv, int D) {
   // One superblock count per split for every request, so requests with
   // longer prefixes get proportionally more splits; chosen by simulating
   // the launch (choose_sbps).
-  const int forced = attn_sbps_override();
-  int nsb_max = 1;
-  for (int r = 0; r < nreq; ++r) nsb_max = std::max(nsb_max, (S[r] + N + kSBK - 1) / kSBK);
-  p.sb_per_split = forced > 0 ? std::min(forced, nsb_max)
-                              : choose_sbps(nreq, S, N, Hq, Hkv, D, p.tiles, p.rows_pad);
+  p.sb_per_split = choose_sbps(nreq, S, N, Hq, Hkv, D, p.tiles, p.rows_pad);
   int wg = 0, sp = 0;
   p.any_split = false;
   for (int r = 0; r < DDTREE_MAX_REQ; ++r) {
@@ -1032,6 +1033,25 @@ AttnPlan attn_plan(int nreq, const int* S, int N, int Hq, int Hkv, int D) {
     p.bytes = p.part_ml_off + rows * 2 * sizeof(float);
   }
   return p;
+}
+
+// The plan cuts request r into at most split_budget(nsb_r) splits and lays
+// out partial rows for the sum of its requests' splits, so the sum of the
+// budgets bounds it; with no request able to split it needs nothing. Both
+// are non-decreasing in every S[r].
+size_t attn_workspace_bound(int nreq, const int* S, int N, int Hq, int Hkv, int D) {
+  const int G = Hq / Hkv, R = N * G;
+  const int tiles = (R + kRowsPerTile - 1) / kRowsPerTile;
+  size_t splits = 0;
+  bool can_split = false;
+  for (int r = 0; r < nreq; ++r) {
+    const int b = split_budget(n_superblocks(S[r], N), Hkv * tiles);
+    splits += (size_t)b;
+    can_split = can_split || b > 1;
+  }
+  if (!can_split) return 0;
+  const size_t rows = splits * Hkv * (size_t)tiles * kRowsPerTile;
+  return rows * D * sizeof(uint16_t) + rows * 2 * sizeof(float);
 }
 
 int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t kv_req_stride,

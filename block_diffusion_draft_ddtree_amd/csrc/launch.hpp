@@ -44,6 +44,9 @@ struct AttnPlan {
   size_t part_o_off, part_ml_off, bytes;
 };
 AttnPlan attn_plan(int nreq, const int* S, int N, int Hq, int Hkv, int D);
+// Workspace that serves attn_plan for these prefix lengths and for every
+// shorter ones (elementwise): non-decreasing in each S[r].
+size_t attn_workspace_bound(int nreq, const int* S, int N, int Hq, int Hkv, int D);
 int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t kv_req_stride,
                 int nreq, const int* S, int S_cap, int N, int Hq, int Hkv, int D, float scale,
                 const uint32_t* anc, int W, uint16_t* out, void* ws, hipStream_t stream);

@@ -352,3 +352,26 @@ def accepted_path(B: int, L: int, g: np.random.Generator) -> np.ndarray:
     a = min(int(g.integers(1, L + 1)), B)
     picks = np.sort(g.choice(np.arange(1, B + 1), size=a, replace=False))
     return np.concatenate([[0], picks]).astype(np.int32)
+
+
+def sweep_accepts(B: int, L: int, rounds: int) -> tuple[np.ndarray, np.ndarray]:
+    """Accepted paths of `rounds` budget-sweep rounds: a_r ~ U[1, L] from a
+    stream that does not depend on B (so the prefix lengths advance the same
+    way at every budget), capped at B, and a_r strictly increasing node ids
+    in [1, B] from a per-budget stream. Returns acc int32 [rounds, L + 1]
+    (acc[r, 0] = 0, unused tail 0) and a int32 [rounds]."""
+    ga = rng("sweep", 0, STREAM_ACCEPT)
+    gp = rng("sweep", B, STREAM_EXTRA)
+    acc = np.zeros((rounds, L + 1), dtype=np.int32)
+    a = np.empty(rounds, dtype=np.int32)
+    for r in range(rounds):
+        a[r] = min(int(ga.integers(1, L + 1)), B)
+        picks = np.sort(gp.choice(np.arange(1, B + 1), size=int(a[r]), replace=False))
+        acc[r, 1:1 + a[r]] = picks
+    return acc, a
+
+
+def sweep_prefix_lengths(S0: int, a: np.ndarray) -> np.ndarray:
+    """Prefix length at the start of each round: S advances by the root plus
+    the accepted tokens of the previous round."""
+    return (S0 + np.concatenate([[0], np.cumsum(1 + a.astype(np.int64))[:-1]])).astype(np.int64)

@@ -167,7 +167,14 @@ int ddtree_build_batched(const float* logp, const int32_t* token, int L, int K, 
  * scale    softmax scale (typically 1/sqrt(D)).
  * anc      uint32 [N, mask_words] as produced by ddtree_build.
  * out      out bf16 [N, Hq, D]; must not alias q, k or v.
- * ws       scratch of at least ddtree_tree_attn_workspace_bytes().
+ * ws       scratch of at least ddtree_tree_attn_workspace_bytes() for this
+ *          S or any larger prefix length: the query is non-decreasing in S,
+ *          so a decode loop can size one workspace at its largest S.
+ *          Holds no state between calls.
+ *
+ * Range: when the key range is split (S + N > 128), every element of V
+ * must satisfy |v| <= 65504 (the fp16 range of the split outputs, which
+ * are convex combinations of V rows); larger values may overflow to inf.
  *
  * out[n,h] = sum_j softmax_j(scale * q[n,h] . k[g,j]) v[g,j] over rows
  * j in [0,S) and j = S + m for every m set in anc[n]; fp32 accumulation and
@@ -197,7 +204,8 @@ int ddtree_tree_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * S           host int32 [R]: request r's prefix length, S[r] + N <= S_cap.
  * anc         uint32 [R, N, mask_words].
  * ws          scratch of at least ddtree_tree_attn_batched_workspace_bytes()
- *             for the same R, S, N, Hq, Hkv, D.
+ *             for the same R, N, Hq, Hkv, D and prefix lengths at least
+ *             S[r] each (the query is non-decreasing in every S[r]).
  * The key range of every request is cut into splits of one common length,
  * so the launch's workgroups follow the total work; request r's output
  * equals ddtree_tree_attn on its own slices. */

@@ -35,12 +35,6 @@ def log_softmax(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def logsumexp_rows(x: np.ndarray) -> np.ndarray:
-    x = np.asarray(x, dtype=np.float64)
-    m = np.max(x, axis=1)
-    return m + np.log(np.sum(np.exp(x - m[:, None]), axis=1))
-
-
 def rank_order(row: np.ndarray) -> np.ndarray:
     """Token ids of one row sorted by (logit descending, id ascending).
 

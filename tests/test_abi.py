@@ -57,6 +57,42 @@ def test_workspace_queries(lib):
         bd.ddtree_tree_attn_workspace_bytes(65, 32, 4, 96, 4096)   # D
 
 
+# Head layouts of the workloads (N, Hq, Hkv, D): tiny; the 8B shape and the
+# budget sweep at B = 64 and 512; the 30B shape at B = 64 and 256 (also the
+# long-context shape).
+WORKLOAD_LAYOUTS = [(17, 4, 2, 64), (65, 32, 8, 128), (513, 32, 8, 128), (65, 32, 4, 128),
+                    (257, 32, 4, 128)]
+
+
+@pytest.mark.parametrize("layout", WORKLOAD_LAYOUTS)
+def test_attn_workspace_monotone_in_prefix(lib, layout):
+    """A workspace sized for prefix length S serves every shorter prefix: the
+    query never asks for more at a smaller S (a decode loop sizes it once at
+    its largest S while S grows by each round's accepted tokens)."""
+    N, Hq, Hkv, D = layout
+    prev = 0
+    for S in range(0, 65537):
+        b = bd.ddtree_tree_attn_workspace_bytes(N, Hq, Hkv, D, S)
+        assert b >= prev, (layout, S, b, prev)
+        prev = b
+
+
+@pytest.mark.parametrize("layout", WORKLOAD_LAYOUTS[1:3])
+def test_batched_attn_workspace_monotone(lib, layout):
+    """The batched query is non-decreasing in each request's prefix length."""
+    import numpy as np
+    N, Hq, Hkv, D = layout
+    g = np.random.default_rng(7)
+    for _ in range(200):
+        R = int(g.integers(1, 9))
+        S = g.integers(0, 20000, size=R)
+        full = bd.ddtree_tree_attn_batched_workspace_bytes(S.tolist(), N, Hq, Hkv, D)
+        r = int(g.integers(0, R))
+        S2 = S.copy()
+        S2[r] = int(g.integers(0, S[r] + 1))
+        assert bd.ddtree_tree_attn_batched_workspace_bytes(S2.tolist(), N, Hq, Hkv, D) <= full
+
+
 def P(v):
     return ctypes.c_void_p(v)
 

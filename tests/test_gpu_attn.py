@@ -111,8 +111,57 @@ def test_planted_keys_order_one_outputs():
     _run(q_bits, q, kv_bits, kv, S, anc, scale=2.0)
 
 
-@pytest.mark.parametrize("name", ["coder30b_b64", "qwen3_8b", "coder30b_b256", "coder30b_b64_deep",
-                                  "sweep_b512"])
+@pytest.mark.parametrize("name", ["coder30b_b64", "qwen3_8b"])
+def test_full_workload_every_element(name):
+    """The metric shapes in full: every output element of one layer (65
+    nodes x 32 heads x 128 dims) against the oracle, through the launch
+    plan bench.py times (7 splits of 5 superblocks at the 30B shape)."""
+    w = synth.WORKLOADS[name]
+    lg = synth.drafter_logits(w)
+    lp, tok = st.topk(lg.x, w.K)
+    tree = ot.build_tree(lp.astype(np.float32), tok, w.B, 0)
+    qkv = synth.attention_inputs(w, layers=1)
+    _run(qkv.q_bits, qkv.q, qkv.kv_bits[0], qkv.kv[0], w.S, tree.anc)
+
+
+def test_planted_keys_through_splits_at_metric_shape():
+    """O(1) outputs through the split path at the 30B shape (32q/4kv heads,
+    D = 128, S = 4096, N = 65; the key range runs as 7 splits whose fp16
+    outputs are merged). Query (n, h) finds a copy of itself among the
+    prefix keys at a row past the first split (rows 640 ... 3760, a
+    different one for every query of a kv-head), or, for one query head per
+    kv-head and node, at the node's own tree row; with the default scale it
+    takes about 90 % of the weight and the rest blends in, so every output
+    is an O(1) mixture that the tolerance resolves. Random tree with depth,
+    every element compared."""
+    N, Hq, Hkv, D, S = 65, 32, 4, 128, 4096
+    q_bits, q, kv_bits, kv, g = _inputs(N, Hq, Hkv, D, S, 11)
+    parent = [-1] + [int(g.integers(max(0, n - 4), n)) for n in range(1, N)]
+    anc = ot.ancestor_mask(parent)
+    kv = kv.copy()
+    G = Hq // Hkv
+    tree_rows = 0
+    for gk in range(Hkv):
+        i = 0
+        for n in range(N):
+            for hh in range(G):
+                h = gk * G + hh
+                if n > 0 and hh == n % G:
+                    kv[0, gk, S + n] = q[n, h]   # the node's own row: always visible
+                    tree_rows += 1
+                else:
+                    kv[0, gk, 640 + 6 * i] = q[n, h]
+                    i += 1
+    assert tree_rows == Hkv * (N - 1)
+    kv_bits = synth.f32_to_bf16_bits(kv)
+    kv = synth.bf16_bits_to_f32(kv_bits)
+    ws = bd.ddtree_tree_attn_workspace_bytes(N, Hq, Hkv, D, S)
+    assert ws > 0  # the key range is split
+    stats = _run(q_bits, q, kv_bits, kv, S, anc)
+    assert stats["max_abs"] < 0.1
+
+
+@pytest.mark.parametrize("name", ["coder30b_b256", "coder30b_b64_deep", "sweep_b512"])
 def test_full_workload_sampled(name):
     w = synth.WORKLOADS[name]
     lg = synth.drafter_logits(w)

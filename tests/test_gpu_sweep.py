@@ -17,7 +17,7 @@ from oracle import attention as oa
 from oracle import softmax_topk as st
 from oracle import tree as ot
 
-from gpu_helpers import assert_attn_close, down, down_bf16_f32, say, up, up_bf16
+from gpu_helpers import assert_attn_close, down, down_bf16_bits, down_bf16_f32, say, up, up_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -100,3 +100,70 @@ def test_topk_and_build_shapes(case):
     np.testing.assert_array_equal(down(depth), tree.depth)
     np.testing.assert_array_equal(down(ntok), tree.token)
     np.testing.assert_array_equal(down(anc).view(np.uint32), tree.anc)
+
+
+def test_budget_sweep_rounds_chained():
+    """Four chained decode rounds of the budget-sweep recipe (B = 32, flat
+    logits, 32q/8kv heads, D = 128, two layers, prefix from 8192): each
+    round writes fresh K/V rows for its tree at rows S..S+N-1, runs top-K,
+    build, both layers' attention at the current S, the walk, and the
+    compaction of a drawn accepted path (a ~ U[1, L]); S then grows by
+    1 + a. One attention workspace serves every round (sized once at the
+    last round's S). Tree, attention (every element), walk and the whole
+    cache after each compaction are compared with the oracle."""
+    from dataclasses import replace
+
+    import torch
+
+    from oracle import commit as oc
+    from block_diffusion_draft_ddtree_amd.round import DraftTreeRound, RoundShape
+
+    rounds = 4
+    w = replace(synth.sweep(32), layers=2)
+    acc_np, a_np = synth.sweep_accepts(w.B, w.L, rounds)
+    S_r = synth.sweep_prefix_lengths(w.S, a_np)
+    S_cap = int(S_r[-1]) + w.N
+    g = synth.rng("test", 803, 0)
+    kv_bits, _ = synth.normal_bf16(g, (w.layers, 2, w.Hkv, S_cap, w.D))
+    kv_dev = up_bf16(kv_bits)
+    shape = RoundShape(w.L, w.V, w.K, w.B, w.Hq, w.Hkv, w.D, w.layers, S_cap)
+    rnd = DraftTreeRound(shape, int(S_r[-1]), "cuda:0")
+    ws0 = rnd.ws_attn.numel()
+    for r in range(rounds):
+        S = int(S_r[r])
+        say(f"sweep decode round={r} S={S} B={w.B}")
+        fresh_bits, _ = synth.normal_bf16(g, (w.layers, 2, w.Hkv, w.N, w.D))
+        kv_bits[:, :, :, S:S + w.N] = fresh_bits
+        kv_dev[:, :, :, S:S + w.N] = up_bf16(fresh_bits)
+        q_bits, q = synth.normal_bf16(g, (w.layers, w.N, w.Hq, w.D))
+        q_dev = up_bf16(q_bits)
+        lg = synth.drafter_logits(w, r)
+        root = int(g.integers(0, w.V))
+        rnd.root_token.fill_(root)
+        rnd.topk(up(lg.x))
+        rnd.build()
+        lp, tok = down(rnd.logp), down(rnd.token)
+        lp_ref, tok_ref = st.topk(lg.x, w.K)
+        np.testing.assert_array_equal(tok, tok_ref)
+        tree = ot.build_tree(lp, tok, w.B, root)
+        np.testing.assert_array_equal(down(rnd.parent), tree.parent)
+        np.testing.assert_array_equal(down(rnd.anc).view(np.uint32), tree.anc)
+        for layer in range(w.layers):
+            rnd.attn(layer, q_dev, kv_dev, S)
+        kv_f = synth.bf16_bits_to_f32(kv_bits)
+        for layer in range(w.layers):
+            ref = oa.tree_attention(q[layer], kv_f[layer, 0], kv_f[layer, 1], S, tree.anc)
+            assert_attn_close(down_bf16_f32(rnd.attn_out[layer]), ref, f"round {r} layer {layer}")
+        tgt = g.integers(0, w.V, size=w.N).astype(np.int32)
+        rnd.walk(up(tgt))
+        acc_w, a_w, bonus = oc.accept_walk(tree.parent, tree.token, tgt, w.L)
+        assert int(down(rnd.n_acc)[0]) == a_w and int(down(rnd.next_bonus)[0]) == bonus
+        acc_d = up(acc_np[r])
+        n_d = up(a_np[r:r + 1])
+        bd.ddtree_kv_compact(kv_dev, S, w.N, w.L, acc_d, n_d)
+        for layer in range(w.layers):
+            kv_bits[layer] = oc.kv_compact(kv_bits[layer], S, acc_np[r][:1 + a_np[r]],
+                                           int(a_np[r]))
+        np.testing.assert_array_equal(down_bf16_bits(kv_dev), kv_bits)
+        torch.cuda.synchronize()
+    assert rnd.ws_attn.numel() == ws0
