@@ -39,6 +39,8 @@ _SIGNATURES = {
     "ddtree_tree_attn_workspace_bytes": (_i32, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "ddtree_tree_attn": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                 _i32, _vp, _vp, _sz, _vp]),
+    "ddtree_tree_attn_noalloc": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                        _vp, _i32, _vp, _vp]),
     "ddtree_target_argmax_workspace_bytes": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "ddtree_target_argmax": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
     "ddtree_budget_select": (_i32, [_vp, _i32, _i32, ctypes.c_double, ctypes.c_double, _vp, _vp,
@@ -198,6 +200,26 @@ def ddtree_tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: int,
         S, S_cap, N, Hq, Hkv, D, scale, _dev(anc, anc.dtype, "anc"), anc.shape[1],
         _dev(out, torch.bfloat16, "out"), _dev(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream)), "ddtree_tree_attn")
+    return out
+
+
+def ddtree_tree_attn_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: int,
+                             anc: torch.Tensor, scale: float | None = None, out=None,
+                             stream=None) -> torch.Tensor:
+    """ddtree_tree_attn with the library's static scratch instead of a
+    workspace (nothing is allocated when `out` is given)."""
+    N, Hq, D = q.shape
+    Hkv, S_cap, Dk = k.shape
+    if Dk != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [Hkv, S_cap, D] with q's D")
+    if anc.dim() != 2 or anc.shape[0] < N:
+        raise ValueError("anc must be [N, mask_words]")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    _check(lib().ddtree_tree_attn_noalloc(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        S, S_cap, N, Hq, Hkv, D, scale, _dev(anc, anc.dtype, "anc"), anc.shape[1],
+        _dev(out, torch.bfloat16, "out"), _stream(stream)), "ddtree_tree_attn_noalloc")
     return out
 
 

@@ -148,6 +148,26 @@ DDT_API int ddtree_tree_attn(const uint16_t* q, const uint16_t* k, const uint16_
                                out, ws, stream);
 }
 
+DDT_API int ddtree_tree_attn_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     int S, int S_cap, int N, int Hq, int Hkv, int D, float scale,
+                                     const uint32_t* anc, int mask_words, uint16_t* out,
+                                     hipStream_t stream) {
+  int st = attn_check(N, Hq, Hkv, D, S);
+  if (st) return st;
+  st = attn_args_check(q, k, v, S_cap, N, scale, anc, mask_words, out);
+  if (st) return st;
+  if ((int64_t)S + N > S_cap) return DDTREE_ERR_INVALID_ARGUMENT;
+  const size_t need = ddt_host::attn_plan(1, &S, N, Hq, Hkv, D).bytes;
+  if (need > DDTREE_NOALLOC_SCRATCH_BYTES) return DDTREE_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (need) {
+    st = ddt_host::attn_static_scratch(&ws);
+    if (st) return st;
+  }
+  return ddt_host::attn_launch(q, k, v, 0, 1, &S, S_cap, N, Hq, Hkv, D, scale, anc, mask_words,
+                               out, ws, stream);
+}
+
 static int attn_batch_check(int R, const int32_t* S, int N, int Hq, int Hkv, int D) {
   if (R < 1 || !S) return DDTREE_ERR_INVALID_ARGUMENT;
   if (R > DDTREE_MAX_REQ) return DDTREE_ERR_UNSUPPORTED;

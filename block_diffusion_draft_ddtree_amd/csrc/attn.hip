@@ -56,7 +56,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <functional>
-#include <vector>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -905,17 +905,17 @@ double model_us(int nreq, const int* S, int N, int Hkv, int D, int tiles, int ro
   const int64_t wgs = splits_total * Hkv * tiles;
   const int64_t per_xcd = (wgs + kXcds - 1) / kXcds;
   double worst = 0.0;
-  std::vector<double> heap;
-  heap.reserve(cus);
+  double heap[kSlots / kXcds];  // a min-heap of the XCD's CU free times
+  double* const heap_end = heap + cus;
   int r = 0, g = 0, split = 0, tile = 0;  // the workgroup at id 0
   for (int x = 0; x < kXcds; ++x) {
-    heap.assign(cus, 0.0);  // every CU free at time 0 (a min-heap of free times)
+    std::fill(heap, heap_end, 0.0);  // every CU free at time 0
     for (int64_t i = 0; i < per_xcd && x * per_xcd + i < wgs; ++i) {
       const int nsb = (S[r] + N + kSBK - 1) / kSBK;
       const double c = std::min(sbps, nsb - split * sbps) * kStepUs + kWgUs;
-      std::pop_heap(heap.begin(), heap.end(), std::greater<double>());
-      heap.back() += c;
-      std::push_heap(heap.begin(), heap.end(), std::greater<double>());
+      std::pop_heap(heap, heap_end, std::greater<double>());
+      heap_end[-1] += c;
+      std::push_heap(heap, heap_end, std::greater<double>());
       // Next id: tile fastest, then split, then kv-head, then request.
       if (++tile == tiles) {
         tile = 0;
@@ -928,7 +928,7 @@ double model_us(int nreq, const int* S, int N, int Hkv, int D, int tiles, int ro
         }
       }
     }
-    worst = std::max(worst, *std::max_element(heap.begin(), heap.end()));
+    worst = std::max(worst, *std::max_element(heap, heap_end));
     if (worst + extra >= cap) return worst + extra;
   }
   return worst + extra;
@@ -965,16 +965,18 @@ int choose_sbps(int nreq, const int* S, int N, int Hq, int Hkv, int D, int tiles
     const int b = split_budget(nsb, Hkv * tiles);
     sbps_min = std::max(sbps_min, (nsb + b - 1) / b);
   }
-  std::vector<int> cand;
-  for (int c = 1; c <= std::min(nsb_max, 64); ++c) cand.push_back(c);
-  for (int k = 1; k <= 64; ++k) cand.push_back((nsb_max + k - 1) / k);
-  cand.push_back(sbps_min);
-  for (int& c : cand) c = std::max(c, sbps_min);
-  std::sort(cand.begin(), cand.end(), std::greater<int>());
-  cand.erase(std::unique(cand.begin(), cand.end()), cand.end());
-  int best = cand.front();
+  // Fixed arrays (no heap allocation on the launch path).
+  int cand[64 + 64 + 1];
+  int nc = 0;
+  for (int c = 1; c <= std::min(nsb_max, 64); ++c) cand[nc++] = c;
+  for (int k = 1; k <= 64; ++k) cand[nc++] = (nsb_max + k - 1) / k;
+  cand[nc++] = sbps_min;
+  for (int i = 0; i < nc; ++i) cand[i] = std::max(cand[i], sbps_min);
+  std::sort(cand, cand + nc, std::greater<int>());
+  nc = (int)(std::unique(cand, cand + nc) - cand);
+  int best = cand[0];
   double best_us = model_us(nreq, S, N, Hkv, D, tiles, rows_pad, best, 1e300);
-  for (size_t i = 1; i < cand.size(); ++i) {
+  for (int i = 1; i < nc; ++i) {
     const double t = model_us(nreq, S, N, Hkv, D, tiles, rows_pad, cand[i], best_us);
     if (t < best_us) {
       best_us = t;
@@ -988,7 +990,28 @@ int choose_sbps(int nreq, const int* S, int N, int Hq, int Hkv, int D, int tiles
 
 }  // namespace
 
+// Split partials of ddtree_tree_attn_noalloc: a device array in the code
+// object, one per GPU. Host code never names it except to look up each
+// device's copy (the name is only a host-side stand-in there).
+static __device__ __align__(256) unsigned char scratch[DDTREE_NOALLOC_SCRATCH_BYTES];
+
 namespace ddt_host {
+
+int attn_static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DDTREE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DDTREE_ERR_HIP;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return DDTREE_OK;
+}
 
 AttnPlan attn_plan(int nreq, const int* S, int N, int Hq, int Hkv, int D) {
   AttnPlan p{};

@@ -44,6 +44,9 @@ struct AttnPlan {
   size_t part_o_off, part_ml_off, bytes;
 };
 AttnPlan attn_plan(int nreq, const int* S, int N, int Hq, int Hkv, int D);
+// Device address of the static scratch array on the current device (looked
+// up once per device); DDTREE_OK or DDTREE_ERR_HIP.
+int attn_static_scratch(void** ptr);
 // Workspace that serves attn_plan for these prefix lengths and for every
 // shorter ones (elementwise): non-decreasing in each S[r].
 size_t attn_workspace_bound(int nreq, const int* S, int N, int Hq, int Hkv, int D);

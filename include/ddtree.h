@@ -70,6 +70,7 @@ typedef enum ddtree_status {
 #define DDTREE_MAX_LK 32768    /* L * K: the whole top-K table sits in LDS   */
 #define DDTREE_MAX_V 4194304   /* vocabulary (1024 chunks of 4096 logits)    */
 #define DDTREE_MAX_REQ 64      /* requests in one batched call               */
+#define DDTREE_NOALLOC_SCRATCH_BYTES (32u << 20) /* ddtree_tree_attn_noalloc's scratch */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* ddtree_status_string(int status);
@@ -190,6 +191,29 @@ int ddtree_tree_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      float scale, const uint32_t* anc, int mask_words,
                      uint16_t* out, void* ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/* ddtree_tree_attn_noalloc -- ddtree_tree_attn with no workspace argument and
+ * no allocation, for callers that cannot allocate device memory or call
+ * hipMalloc: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.
+ *
+ * Arguments, semantics and results are those of ddtree_tree_attn (same
+ * kernels, same launch plan, bit-identical output). The split partials go
+ * to a static device array of DDTREE_NOALLOC_SCRATCH_BYTES (32 MiB) that
+ * the library holds on every GPU it runs on until the process ends; its
+ * address is looked up once per device, on the first call that needs it
+ * with that device current. `stream` must belong to the current device.
+ * Returns DDTREE_ERR_WORKSPACE_TOO_SMALL (nothing enqueued) when the plan
+ * needs more than the array, i.e. when ddtree_tree_attn would need a
+ * workspace larger than 32 MiB for this shape and S.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (nothing in it needs clearing): calls that overlap on one GPU
+ * (other streams, other threads) race and must be serialised by the
+ * caller. */
+int ddtree_tree_attn_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             int S, int S_cap, int N, int Hq, int Hkv, int D,
+                             float scale, const uint32_t* anc, int mask_words,
+                             uint16_t* out, hipStream_t stream);
 
 /* ddtree_tree_attn_batched -- ddtree_tree_attn for R requests in one launch
  * (1 <= R <= DDTREE_MAX_REQ), each with its own tree and its own prefix

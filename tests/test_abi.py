@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(bd.EXPORTS)
@@ -135,6 +135,25 @@ def test_attn_validation(lib):
     assert f(*args(D=96, ws=1 << 40)) == bd.DDTREE_ERR_UNSUPPORTED
     assert f(*args(scale=-1.0, ws=1 << 40)) == bd.DDTREE_ERR_INVALID_ARGUMENT
     assert f(*args(N=1026, S_cap=1 << 20, W=40, ws=1 << 40)) == bd.DDTREE_ERR_UNSUPPORTED
+
+
+def test_attn_noalloc_validation(lib):
+    """The allocation-free attention checks its arguments like ddtree_tree_attn
+    and refuses, before any HIP call, a plan whose split partials exceed its
+    static scratch (DDTREE_NOALLOC_SCRATCH_BYTES = 32 MiB)."""
+    f = lib.ddtree_tree_attn_noalloc
+    args = lambda S, S_cap, N, Hq, Hkv, D, scale=0.1, W=1: (
+        P(FAKE), P(FAKE), P(FAKE), S, S_cap, N, Hq, Hkv, D, ctypes.c_float(scale), P(FAKE), W,
+        P(FAKE), None)
+    assert f(*args(100, 150, 65, 32, 4, 96, W=3)) == bd.DDTREE_ERR_UNSUPPORTED        # D
+    assert f(*args(100, 150, 65, 30, 4, 128, W=3)) == bd.DDTREE_ERR_INVALID_ARGUMENT  # Hq % Hkv
+    assert f(*args(100, 150, 65, 32, 4, 128, W=2)) == bd.DDTREE_ERR_INVALID_ARGUMENT  # mask words
+    assert f(*args(100, 160, 65, 32, 4, 128, W=3)) == bd.DDTREE_ERR_INVALID_ARGUMENT  # S + N > S_cap
+    assert f(*args(100, 200, 65, 32, 4, 128, 0.0, W=3)) == bd.DDTREE_ERR_INVALID_ARGUMENT  # scale
+    # The largest tree at a long prefix needs more split partials than the
+    # static scratch holds (its workspace query says so too).
+    assert bd.ddtree_tree_attn_workspace_bytes(1025, 32, 8, 128, 60000) > 32 << 20
+    assert f(*args(60000, 61025, 1025, 32, 8, 128, W=33)) == bd.DDTREE_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_walk_and_compact_validation(lib):
