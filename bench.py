@@ -293,6 +293,53 @@ def main():
     a_acc = int(rnd.n_acc.cpu()[0])
     depth = rnd.depth.cpu().numpy()
 
+    # The round consuming the cost-aware budget on the device: after the
+    # build, ddtree_budget_select picks the budget from the build's scores
+    # (time model fitted to the autobench page) and ddtree_tree_prune keeps
+    # that tree; attention, walk and compaction then work on the kept nodes.
+    # Three graph replays per step, as the main round.
+    budget_round = None
+    if graphs is not None:
+        bparts = (lambda: (rnd.topk(logits), rnd.build(), rnd.select_budget(BUDGET_T0, BUDGET_T1),
+                           rnd.prune()),
+                  lambda: [rnd.attn(layer, q, kv, w.S) for layer in range(w.layers)],
+                  lambda: (rnd.walk(tgt), rnd.compact(kv, w.S)))
+        for part in bparts:
+            part()
+        torch.cuda.synchronize()
+        bgraphs = []
+        for part in bparts:
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                part()
+            bgraphs.append(gph)
+        for _ in range(args.warmup):
+            for gph in bgraphs:
+                gph.replay()
+        pairs = [(ev(), ev()) for _ in range(args.steps)]
+        e0, e1 = ev(), ev()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for a, b in pairs:
+            bgraphs[0].replay()
+            a.record(stream)
+            bgraphs[1].replay()
+            b.record(stream)
+            bgraphs[2].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kept = int(rnd.budget.cpu()[0]) + 1
+        budget_round = {"budget": kept - 1, "kept_nodes": kept,
+                        "round_us": round(e0.elapsed_time(e1) * 1e3 / args.steps, 2),
+                        "tree_attn_us": round(float(np.mean(
+                            [a.elapsed_time(b) * 1e3 / w.layers for a, b in pairs])), 3),
+                        "accepted": int(rnd.n_acc.cpu()[0])}
+        del bgraphs
+        # Rebuild the full tree for what follows.
+        rnd.topk(logits)
+        rnd.build()
+        torch.cuda.synchronize()
+
     nbytes, flops = attn_work(w, depth)
     hbm_gbs = nbytes / (attn_us * 1e-6) / 1e9
     tflops = flops / (attn_us * 1e-6) / 1e12
@@ -341,6 +388,8 @@ def main():
         "depth_hist": np.bincount(depth).tolist(),
         "roofline": roof,
     }
+    if budget_round is not None:
+        result["budget_round"] = budget_round
 
     if args.batch_requests > 0:
         result["batched"] = batched_leg(w, args.batch_requests, args.steps, args.warmup,

@@ -47,6 +47,7 @@ _SIGNATURES = {
                                     _vp]),
     "ddtree_target_sample": (_i32, [_vp, _i32, _i64, _i32, _i32, _f32, _u64, _u64, _vp, _vp, _sz,
                                     _vp]),
+    "ddtree_tree_prune": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp]),
     "ddtree_accept_walk": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "ddtree_kv_compact": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "ddtree_build_batched": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -280,6 +281,18 @@ def ddtree_budget_select(score: torch.Tensor, B_max: int, t0: float, t1: float, 
                                       _dev(budget, torch.int32, "budget"), _stream(stream)),
            "ddtree_budget_select")
     return budget, expected
+
+
+def ddtree_tree_prune(budget: torch.Tensor, parent: torch.Tensor, anc: torch.Tensor,
+                      stream=None) -> None:
+    """In place: nodes past budget[0] get parent -1 and an empty mask row."""
+    N = parent.shape[0]
+    if anc.dim() != 2 or anc.shape[0] != N:
+        raise ValueError("anc must be [N, mask_words]")
+    _check(lib().ddtree_tree_prune(_dev(budget, torch.int32, "budget"), N,
+                                   _dev(parent, torch.int32, "parent"),
+                                   _dev(anc, anc.dtype, "anc"), anc.shape[1], _stream(stream)),
+           "ddtree_tree_prune")
 
 
 def ddtree_accept_walk(parent: torch.Tensor, node_token: torch.Tensor, L: int,

@@ -269,6 +269,14 @@ DDT_API int ddtree_budget_select(const float* score, int B_max, int B_min, doubl
   return ddt_host::budget_launch(score, B_max, B_min, t0, t1, expected, budget, stream);
 }
 
+DDT_API int ddtree_tree_prune(const int32_t* budget, int N, int32_t* parent, uint32_t* anc,
+                              int mask_words, hipStream_t stream) {
+  if (N < 1 || !budget || !parent || !anc) return DDTREE_ERR_INVALID_ARGUMENT;
+  if (N > DDTREE_MAX_B + 1) return DDTREE_ERR_UNSUPPORTED;
+  if ((int64_t)mask_words * 32 < N) return DDTREE_ERR_INVALID_ARGUMENT;
+  return ddt_host::prune_launch(budget, N, parent, anc, mask_words, stream);
+}
+
 static int walk_check(const int32_t* parent, const int32_t* node_token, int N, int L, int R,
                       const int32_t* target, int32_t* acc, int32_t* n_acc, int32_t* next_bonus) {
   if (N < 1 || L < 1 || R < 1) return DDTREE_ERR_INVALID_ARGUMENT;

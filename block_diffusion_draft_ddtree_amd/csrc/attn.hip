@@ -544,6 +544,17 @@ __device__ __forceinline__ void attn_workgroup(
       mrows[i] = anc[(int64_t)(rr / G) * W + w];
     }
   }
+  // A pruned tree (ddtree_tree_prune) has empty ancestor rows for the nodes
+  // it dropped: a tile none of whose nodes keeps its own bit has nothing to
+  // compute. The bits load with the prologue's copies and are checked once
+  // everything has landed (below).
+  uint32_t own = 0u;
+  {
+    const int n_first = tile_row0 / G;
+    const int n_last = min(R - 1, tile_row0 + kRowsPerTile - 1) / G;
+    const int n = n_first + lane;  // at most 64 nodes per tile
+    if (n <= n_last) own = (anc[(int64_t)n * W + (n >> 5)] >> (n & 31)) & 1u;
+  }
   const uint32_t* myrow = mrows + (rw * 32 + j) * Wn;
   auto vis_of = [&](int key0) {
     if (key0 + kBK <= S) return ~0u;
@@ -565,6 +576,9 @@ __device__ __forceinline__ void attn_workgroup(
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // Every copy has landed: a tile of pruned nodes only can leave (all its
+  // waves see the same bits, so none waits at a later barrier).
+  if (!ddt::ballot(own != 0u)) return;
   // Q^T operands of the wave's 32 rows, read like a K operand; then a
   // barrier before step 0 copies into k1.
   bf16x8 qf[C::KS];
@@ -774,6 +788,7 @@ template <int D>
 __device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
                                              const float* __restrict__ part_ml, int splits,
                                              int split_base, int N, int Hq, int Hkv, int tiles,
+                                             const uint32_t* __restrict__ anc, int W,
                                              uint16_t* __restrict__ out) {
   constexpr int DT = D / 32;
   const int t = blockIdx.x * 256 + threadIdx.x;
@@ -787,6 +802,12 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
   const int j = lane & 31, h = lane >> 5;
   const int rho = tile * kRowsPerTile + rw * 32 + j;
   if (rho >= R) return;
+  {
+    // Rows of nodes a pruned tree dropped have no partials (their tile may
+    // not have run) and no output.
+    const int n = rho / G;
+    if (!((anc[(int64_t)n * W + (n >> 5)] >> (n & 31)) & 1u)) return;
+  }
   const uint2* po = reinterpret_cast<const uint2*>(part_o);
   const float2* pml = reinterpret_cast<const float2*>(part_ml);
   float M = -INFINITY, L = 0.f;
@@ -837,8 +858,9 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int N,
-    int Hq, int Hkv, int tiles, uint16_t* __restrict__ out) {
-  combine_rows<D>(part_o, part_ml, splits, 0, N, Hq, Hkv, tiles, out);
+    int Hq, int Hkv, int tiles, const uint32_t* __restrict__ anc, int W,
+    uint16_t* __restrict__ out) {
+  combine_rows<D>(part_o, part_ml, splits, 0, N, Hq, Hkv, tiles, anc, W, out);
 }
 
 // blockIdx.y is the request; one that ran as a single split wrote its
@@ -847,13 +869,13 @@ template <int D>
 __global__ __launch_bounds__(256) void tree_attn_batched_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, ReqInts S_of,
     ReqInts wg_end, int sb_per_split, int N, int Hq, int Hkv, int tiles,
-    uint16_t* __restrict__ out) {
+    const uint32_t* __restrict__ anc, int W, uint16_t* __restrict__ out) {
   const int req = blockIdx.y;
   const int splits = req_splits(S_of.v[req], N, sb_per_split);
   if (splits == 1) return;
   const int split_base = req ? wg_end.v[req - 1] / (Hkv * tiles) : 0;
   combine_rows<D>(part_o, part_ml, splits, split_base, N, Hq, Hkv, tiles,
-                  out + (int64_t)req * N * Hq * D);
+                  anc + (int64_t)req * N * W, W, out + (int64_t)req * N * Hq * D);
 }
 
 // Workgroups resident at once: one per CU (LDS holds one).
@@ -1112,17 +1134,17 @@ int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t
   if (nreq == 1) {
     if (D == 128)
       hipLaunchKernelGGL(tree_attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, po, pml,
-                         p.splits.v[0], N, Hq, Hkv, p.tiles, out);
+                         p.splits.v[0], N, Hq, Hkv, p.tiles, anc, W, out);
     else
       hipLaunchKernelGGL(tree_attn_combine_kernel<64>, cgrid, dim3(256), 0, stream, po, pml,
-                         p.splits.v[0], N, Hq, Hkv, p.tiles, out);
+                         p.splits.v[0], N, Hq, Hkv, p.tiles, anc, W, out);
   } else {
     if (D == 128)
       hipLaunchKernelGGL(tree_attn_batched_combine_kernel<128>, cgrid, dim3(256), 0, stream, po,
-                         pml, p.S, p.wg_end, p.sb_per_split, N, Hq, Hkv, p.tiles, out);
+                         pml, p.S, p.wg_end, p.sb_per_split, N, Hq, Hkv, p.tiles, anc, W, out);
     else
       hipLaunchKernelGGL(tree_attn_batched_combine_kernel<64>, cgrid, dim3(256), 0, stream, po,
-                         pml, p.S, p.wg_end, p.sb_per_split, N, Hq, Hkv, p.tiles, out);
+                         pml, p.S, p.wg_end, p.sb_per_split, N, Hq, Hkv, p.tiles, anc, W, out);
   }
   return launch_status(hipGetLastError());
 }

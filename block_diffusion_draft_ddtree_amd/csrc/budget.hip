@@ -73,9 +73,30 @@ __global__ __launch_bounds__(kThreads) void budget_kernel(const float* __restric
   }
 }
 
+// Nodes past the budget leave the tree: no parent (no walk reaches them)
+// and an empty ancestor row (the attention skips tiles of such rows). One
+// thread per mask word.
+__global__ __launch_bounds__(256) void prune_kernel(const int32_t* __restrict__ budget, int N,
+                                                    int32_t* __restrict__ parent,
+                                                    uint32_t* __restrict__ anc, int W) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= N * W) return;
+  const int n = i / W;
+  if (n <= budget[0]) return;
+  anc[i] = 0u;
+  if (i % W == 0) parent[n] = -1;
+}
+
 }  // namespace
 
 namespace ddt_host {
+
+int prune_launch(const int32_t* budget, int N, int32_t* parent, uint32_t* anc, int W,
+                 hipStream_t stream) {
+  hipLaunchKernelGGL(prune_kernel, dim3((N * W + 255) / 256), dim3(256), 0, stream, budget, N,
+                     parent, anc, W);
+  return launch_status(hipGetLastError());
+}
 
 int budget_launch(const float* score, int B_max, int B_min, double t0, double t1,
                   float* expected, int32_t* budget, hipStream_t stream) {

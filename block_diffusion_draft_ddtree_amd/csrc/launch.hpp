@@ -54,6 +54,9 @@ int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t
                 int nreq, const int* S, int S_cap, int N, int Hq, int Hkv, int D, float scale,
                 const uint32_t* anc, int W, uint16_t* out, void* ws, hipStream_t stream);
 
+int prune_launch(const int32_t* budget, int N, int32_t* parent, uint32_t* anc, int W,
+                 hipStream_t stream);
+
 size_t argmax_workspace_bytes(int N, int V, int dtype_bytes);
 int argmax_launch(const void* logits, int bf16, int64_t row_stride, int N, int V, void* ws,
                   int32_t* out, hipStream_t stream);

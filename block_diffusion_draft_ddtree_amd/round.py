@@ -82,6 +82,11 @@ class DraftTreeRound:
         return bd.ddtree_budget_select(self.score, self.shape.B, t0, t1, B_min,
                                        expected=self.expected_accept, budget=self.budget)
 
+    def prune(self):
+        """Keep the budget[0]-tree (set by select_budget) inside this round's
+        tree: the walk and the attention then skip the dropped nodes."""
+        bd.ddtree_tree_prune(self.budget, self.parent, self.anc)
+
     def target_argmax(self, target_logits):
         """bf16 [N, V] target head logits -> the target's greedy token per node."""
         return bd.ddtree_target_argmax(target_logits, out=self.target_choice, ws=self.ws_argmax)

@@ -335,6 +335,29 @@ int ddtree_budget_select(const float* score, int B_max, int B_min, double t0, do
                          float* expected, int32_t* budget, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * ddtree_tree_prune -- keep the budget-B' tree inside a built tree.
+ *
+ * Source: [DD] section 2, Propositions 2-3 (best-first pops come in score
+ * order, so the budget-B' tree is the first B' + 1 nodes of a build with a
+ * larger budget); [AB] results and notes (the budget optimum; the verifier
+ * should spend work only on the nodes it keeps).
+ *
+ * budget     device int32 [1]: B', 0 <= B' (e.g. ddtree_budget_select's
+ *            output); values >= N - 1 keep every node.
+ * N          nodes of the built tree, 1 <= N <= DDTREE_MAX_B + 1.
+ * parent     in/out int32 [N]: parent[n] = -1 for every n > B', so that
+ *            ddtree_accept_walk never reaches them.
+ * anc        in/out uint32 [N, mask_words]: rows of nodes n > B' cleared.
+ * With the rows cleared, ddtree_tree_attn skips the query tiles that hold
+ * only pruned nodes; the output rows of pruned nodes are unspecified. The
+ * kept nodes' rows, parents and mask rows are those of a build with budget
+ * B' (prefix-closed: every kept node's ancestors are kept), so the walk and
+ * the kept outputs equal those of the budget-B' round.
+ * ---------------------------------------------------------------------- */
+int ddtree_tree_prune(const int32_t* budget, int N, int32_t* parent, uint32_t* anc,
+                      int mask_words, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * ddtree_accept_walk -- greedy verification walk down the tree.
  *
  * Source: [DD] section 6 (walk state machine: follow the child whose token

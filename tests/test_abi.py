@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(bd.EXPORTS)
@@ -154,6 +154,14 @@ def test_attn_noalloc_validation(lib):
     # static scratch holds (its workspace query says so too).
     assert bd.ddtree_tree_attn_workspace_bytes(1025, 32, 8, 128, 60000) > 32 << 20
     assert f(*args(60000, 61025, 1025, 32, 8, 128, W=33)) == bd.DDTREE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_prune_validation(lib):
+    f = lib.ddtree_tree_prune
+    assert f(P(FAKE), 65, P(FAKE), P(FAKE), 2, None) == bd.DDTREE_ERR_INVALID_ARGUMENT  # words
+    assert f(None, 65, P(FAKE), P(FAKE), 3, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert f(P(FAKE), 0, P(FAKE), P(FAKE), 1, None) == bd.DDTREE_ERR_INVALID_ARGUMENT
+    assert f(P(FAKE), 1026, P(FAKE), P(FAKE), 33, None) == bd.DDTREE_ERR_UNSUPPORTED
 
 
 def test_walk_and_compact_validation(lib):

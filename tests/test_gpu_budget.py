@@ -104,3 +104,79 @@ def test_on_device_build_scores():
     s_np = score.cpu().numpy()
     np.testing.assert_allclose(e.cpu().numpy(), ob.expected_accept(s_np), rtol=2e-7, atol=1e-30)
     assert int(b.cpu()[0]) == ob.select_budget(s_np, _T0, _T1, 1, B_max)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_pruned_round_equals_the_budget_tree(seed):
+    """The round consumes the cost-aware budget on the device: build with
+    budget 64, ddtree_budget_select, ddtree_tree_prune, then the attention
+    and the walk on the pruned tree. The kept nodes' parents and mask rows,
+    their attention rows and the walk (with a target planted along the
+    deepest path of the full tree, so that it runs past the budget) equal
+    the oracle's on a build with the selected budget."""
+    from oracle import attention as oa
+    from oracle import commit as oc
+    from oracle import softmax_topk as st
+    from oracle import tree as ot
+
+    from gpu_helpers import assert_attn_close, down, down_bf16_f32, up, up_bf16
+
+    g = synth.rng("test", 693, seed)
+    L, V, K, B_max = 8, 512, 8, 64
+    N = B_max + 1
+    W = (N + 31) // 32
+    x = synth.deep_logits(L, V, g).astype(np.float32)
+    root = int(g.integers(0, V))
+    say(f"pruned round seed={seed}")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    logp = torch.empty((L, K), dtype=torch.float32, device="cuda")
+    token = torch.empty((L, K), **i32)
+    bd.ddtree_topk(up(x), K, logp, token)
+    lp_ref, tok_ref = st.topk(x, K)
+    np.testing.assert_array_equal(down(token), tok_ref)
+    # The oracle builds from the device's [L, K] table (the tree parity rule).
+    full = ot.build_tree(down(logp), down(token), B_max, root)
+    # A time model whose optimum lies well inside (0, B_max).
+    for t1 in (0.02, 0.05, 0.1, 0.2, 0.5, 1.0):
+        want_b = ob.select_budget(full.score, 1.0, t1, 1, B_max)
+        if 2 <= want_b <= B_max - 8:
+            break
+    assert 2 <= want_b <= B_max - 8
+    parent, depth, ntok = torch.empty(N, **i32), torch.empty(N, **i32), torch.empty(N, **i32)
+    score = torch.empty(N, dtype=torch.float32, device="cuda")
+    anc = torch.empty((N, W), **i32)
+    bd.ddtree_build(logp, token, B_max, up(np.array([root], np.int32)), W, parent, depth, ntok,
+                    score, anc)
+    b, _ = bd.ddtree_budget_select(score, B_max, 1.0, t1, 1)
+    bd.ddtree_tree_prune(b, parent, anc)
+    Bp = int(down(b)[0])
+    assert Bp == want_b
+    Np = Bp + 1
+    kept = ot.build_tree(down(logp), down(token), Bp, root, mask_words=W)
+    got_parent = down(parent)
+    np.testing.assert_array_equal(got_parent[:Np], kept.parent)
+    assert (got_parent[Np:] == -1).all()
+    got_anc = down(anc).view(np.uint32)
+    np.testing.assert_array_equal(got_anc[:Np], kept.anc)
+    assert (got_anc[Np:] == 0).all()
+    # Attention of the pruned tree: the kept rows against the oracle on the
+    # budget-B' tree (its tree rows are the first Np of the cache's).
+    Hq, Hkv, D, S = 8, 2, 128, 200
+    q_bits, q = synth.normal_bf16(g, (N, Hq, D))
+    kv_bits, kv = synth.normal_bf16(g, (2, Hkv, S + N, D))
+    kvd = up_bf16(kv_bits)
+    out = bd.ddtree_tree_attn(up_bf16(q_bits), kvd[0], kvd[1], S, anc)
+    ref = oa.tree_attention(q[:Np], kv[0], kv[1], S, kept.anc)
+    assert_attn_close(down_bf16_f32(out)[:Np], ref, f"pruned tree, {Np} nodes")
+    # The walk: a target planted along the full tree's path to its last pop,
+    # which the budget drops.
+    path = [N - 1]
+    while path[-1] != 0:
+        path.append(int(full.parent[path[-1]]))
+    tgt = synth.target_argmax_planted(full.parent, full.token, path[::-1], V, g)
+    acc, n_acc, bonus = bd.ddtree_accept_walk(parent, ntok, L, up(tgt))
+    want_acc, want_a, want_bonus = oc.accept_walk(kept.parent, kept.token, tgt[:Np], L)
+    assert int(down(n_acc)[0]) == want_a
+    np.testing.assert_array_equal(down(acc)[: want_a + 1], want_acc[: want_a + 1])
+    assert int(down(bonus)[0]) == want_bonus
+    assert want_a < int(full.depth[N - 1])  # the budget cut the planted path
