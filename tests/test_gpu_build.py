@@ -136,3 +136,16 @@ def test_max_table():
     _compare(lp, tok, 1024)
     lp, tok = synth.sorted_logp_table(16, 1024, 200000, g, scale=3.0)
     _compare(lp, tok, 64)
+
+
+def test_table_at_the_lds_limit():
+    """L * K = 32768 (L = 32, K = 1024), the largest table the build keeps in
+    LDS (DDTREE_MAX_LK), with a narrow and a wide spread of log-probs (trees
+    of depth 8 and 9 at budget 192; a larger budget makes the sort-based
+    oracle take minutes)."""
+    g = synth.rng("test", 631, 0)
+    lp, tok = synth.sorted_logp_table(32, 1024, 200000, g, scale=0.05)
+    ref = _compare(lp, tok, 192)
+    assert ref.depth.max() >= 8
+    lp, tok = synth.sorted_logp_table(32, 1024, 200000, g, scale=3.0)
+    _compare(lp, tok, 192)
