@@ -101,6 +101,8 @@ def parse():
                     help="requests in the batched-round leg (0 skips it)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workload shapes (8B, 30B at B = 256, long context)")
+    ap.add_argument("--no-budget-round", action="store_true",
+                    help="skip the round that selects and prunes the budget on the device")
     ap.add_argument("--sweep-rounds", type=int, default=1000,
                     help="decode rounds per budget in the budget-sweep leg (0 skips it)")
     return ap.parse_args()
@@ -299,7 +301,7 @@ def main():
     # that tree; attention, walk and compaction then work on the kept nodes.
     # Three graph replays per step, as the main round.
     budget_round = None
-    if graphs is not None:
+    if graphs is not None and not args.no_budget_round:
         bparts = (lambda: (rnd.topk(logits), rnd.build(), rnd.select_budget(BUDGET_T0, BUDGET_T1),
                            rnd.prune()),
                   lambda: [rnd.attn(layer, q, kv, w.S) for layer in range(w.layers)],
