@@ -802,12 +802,12 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
   const int j = lane & 31, h = lane >> 5;
   const int rho = tile * kRowsPerTile + rw * 32 + j;
   if (rho >= R) return;
-  {
-    // Rows of nodes a pruned tree dropped have no partials (their tile may
-    // not have run) and no output.
-    const int n = rho / G;
-    if (!((anc[(int64_t)n * W + (n >> 5)] >> (n & 31)) & 1u)) return;
-  }
+  // Rows of nodes a pruned tree dropped have no partials (their tile may not
+  // have run) and no output. The check's load goes out with the partials'
+  // loads and is tested before the store (a dropped row merges whatever the
+  // workspace holds and discards it), so it adds no round trip.
+  const int node = rho / G;
+  const uint32_t own_word = anc[(int64_t)node * W + (node >> 5)];
   const uint2* po = reinterpret_cast<const uint2*>(part_o);
   const float2* pml = reinterpret_cast<const float2*>(part_ml);
   float M = -INFINITY, L = 0.f;
@@ -846,8 +846,9 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
     }
     M = bm;
   }
+  if (!((own_word >> (node & 31)) & 1u)) return;
   const float inv = 1.0f / L;
-  const int node = rho / G, hq = g * G + rho % G;
+  const int hq = g * G + rho % G;
   const int d0 = 32 * dt + 8 * qd + 4 * h;
   uint2 pk;
   pk.x = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);

@@ -18,8 +18,8 @@ int launch_status(hipError_t e);
 
 // ddtree_topk: chunk kernel + merge kernel; workspace carve-up.
 struct TopkPlan {
-  int C, cap, idx_passes;
-  size_t stats_off, counts_off, candx_off, candi_off, bytes;
+  int C, cap, idx_passes, q;
+  size_t stats_off, bounds_off, counts_off, candx_off, candi_off, bytes;
 };
 TopkPlan topk_plan(int L, int V, int K);
 int topk_launch(const float* logits, int64_t stride, int L, int V, int K, float* logp,

@@ -35,6 +35,114 @@ constexpr int kMergeThreads = 1024;
 constexpr int kSurvCap = 16384;                      // survivors selected in LDS (128 KB)
 constexpr int kLoadBatch = 8;                        // candidates loaded per thread at once
 constexpr int kRankAllMax = 256;                     // survivors ranked all against all
+constexpr int kBounds = 7;                           // per-chunk bounds: r = 1, 2, 4, ..., 64
+constexpr int kMaxCap = DDTREE_MAX_K + kLooseExtra;  // candidate slots per chunk
+
+// A workgroup barrier for data exchanged through LDS only: waits for this
+// wave's LDS operations, not for its global loads and stores (which
+// __syncthreads would wait for as well). Every barrier in these kernels
+// exchanges LDS data only.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unchanged
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The value of lane (lane ^ J), J a power of two below 64: DPP within rows
+// of 16 lanes, the permlane swaps across them (no LDS round trip).
+template <int J>
+__device__ __forceinline__ float xor_lane(float v) {
+  const int iv = __float_as_int(v);
+  const int lane = (int)__lane_id();
+  if constexpr (J == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(iv, iv, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (J == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(iv, iv, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (J == 4) {
+    const int up = __builtin_amdgcn_update_dpp(iv, iv, 0x104, 0xF, 0xF, false);  // lane + 4
+    const int dn = __builtin_amdgcn_update_dpp(iv, iv, 0x114, 0xF, 0xF, false);  // lane - 4
+    return __int_as_float((lane & 4) ? dn : up);
+  } else if constexpr (J == 8) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(iv, iv, 0x128, 0xF, 0xF, false));
+  } else if constexpr (J == 16) {
+    // Swapping with itself leaves rows (0, 0, 2, 2) in the first result
+    // and rows (1, 1, 3, 3) in the second.
+    const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)iv, (uint32_t)iv, false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(J == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)iv, (uint32_t)iv, false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
+}
+
+// One compare-exchange stage of a bitonic sort over the wave (largest
+// first): blocks of K lanes, partners J apart.
+template <int K, int J>
+__device__ __forceinline__ float bitonic_stage(float v) {
+  const int lane = (int)__lane_id();
+  const float p = xor_lane<J>(v);
+  const bool keep_max = ((lane & J) == 0) == ((lane & K) == 0);
+  return keep_max ? fmaxf(v, p) : fminf(v, p);
+}
+
+// The wave's 64 values sorted, largest on lane 0.
+__device__ __forceinline__ float wave_sort_desc(float v) {
+  v = bitonic_stage<2, 1>(v);
+  v = bitonic_stage<4, 2>(v);
+  v = bitonic_stage<4, 1>(v);
+  v = bitonic_stage<8, 4>(v);
+  v = bitonic_stage<8, 2>(v);
+  v = bitonic_stage<8, 1>(v);
+  v = bitonic_stage<16, 8>(v);
+  v = bitonic_stage<16, 4>(v);
+  v = bitonic_stage<16, 2>(v);
+  v = bitonic_stage<16, 1>(v);
+  v = bitonic_stage<32, 16>(v);
+  v = bitonic_stage<32, 8>(v);
+  v = bitonic_stage<32, 4>(v);
+  v = bitonic_stage<32, 2>(v);
+  v = bitonic_stage<32, 1>(v);
+  v = bitonic_stage<64, 32>(v);
+  v = bitonic_stage<64, 16>(v);
+  v = bitonic_stage<64, 8>(v);
+  v = bitonic_stage<64, 4>(v);
+  v = bitonic_stage<64, 2>(v);
+  v = bitonic_stage<64, 1>(v);
+  return v;
+}
+
+// The q-th largest (q = 1, 2, 4, 8 or 16) of a thread's 16 values, whose
+// largest is xmax.
+__device__ __forceinline__ float qth_largest(const float (&x)[16], int q, float xmax) {
+  if (q == 1) return xmax;
+  if (q == 16) {
+    float m = x[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) m = fminf(m, x[j]);
+    return m;
+  }
+  // Bitonic sort of the 16 values (largest first), then pick.
+  float y[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) y[j] = x[j];
+#pragma unroll
+  for (int k = 2; k <= 16; k <<= 1)
+#pragma unroll
+    for (int jj = k >> 1; jj > 0; jj >>= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int l = i ^ jj;
+        if (l > i) {
+          const float a = y[i], b = y[l];
+          const bool desc = (i & k) == 0;
+          y[i] = desc ? fmaxf(a, b) : fminf(a, b);
+          y[l] = desc ? fminf(a, b) : fmaxf(a, b);
+        }
+      }
+  return q == 2 ? y[1] : q == 4 ? y[3] : y[7];
+}
 
 // Larger digit = closer to the reference maximum (monotone in x).
 __device__ __forceinline__ uint32_t rel_digit(float ref_max, float x) {
@@ -42,37 +150,6 @@ __device__ __forceinline__ uint32_t rel_digit(float ref_max, float x) {
   uint32_t b = (__float_as_uint(y) - 0x3F800000u) >> 19;
   b = b > 255u ? 255u : b;
   return 255u - b;
-}
-
-// a before b in rank order: larger logit first, then smaller id.
-__device__ __forceinline__ bool beats(float xa, int ia, float xb, int ib) {
-  return xa > xb || (xa == xb && ia < ib);
-}
-
-// Rank of (xt, it) among xs/is[0, n) (how many beat it), n a multiple of 16
-// (pad with sentinels that beat nothing: -inf logit, largest id). Sixteen
-// candidates per iteration with 16-byte LDS reads, so the reads of an
-// iteration are in flight together.
-__device__ __forceinline__ int rank_among(const float* xs, const int* is, int n, float xt,
-                                          int it) {
-  int rank = 0;
-  for (int u = 0; u < n; u += 16) {
-    float4 xa[4];
-    int4 ia[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      xa[q] = *reinterpret_cast<const float4*>(xs + u + 4 * q);
-      ia[q] = *reinterpret_cast<const int4*>(is + u + 4 * q);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      rank += beats(xa[q].x, ia[q].x, xt, it);
-      rank += beats(xa[q].y, ia[q].y, xt, it);
-      rank += beats(xa[q].z, ia[q].z, xt, it);
-      rank += beats(xa[q].w, ia[q].w, xt, it);
-    }
-  }
-  return rank;
 }
 
 // Radix-select histograms, three of them in rotation: pass p counts into
@@ -167,7 +244,7 @@ __device__ __forceinline__ void refine_bucket(SelShared& sh, uint32_t need, int 
     sh.kmax[wave] = kx;
     sh.kmin[wave] = kn;
   }
-  __syncthreads();
+  lds_barrier();
   kx = 0u;
   kn = 0xFFFFFFFFu;
   for (int w = 0; w < nw; ++w) {
@@ -191,7 +268,7 @@ __device__ __forceinline__ void refine_bucket(SelShared& sh, uint32_t need, int 
         if ((k & mask) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1u);
       }
     }
-    __syncthreads();
+    lds_barrier();
     const DigitSel ds = find_digit(h, need);
     prefix |= ds.digit << shift;
     mask |= dmask << shift;
@@ -214,7 +291,7 @@ __device__ __forceinline__ void refine_bucket(SelShared& sh, uint32_t need, int 
           if ((ik & im) == ip) atomicAdd(&h[(ik >> shift) & 255u], 1u);
         }
       }
-      __syncthreads();
+      lds_barrier();
       const DigitSel ds = find_digit(h, need);
       ip |= ds.digit << shift;
       im |= 255u << shift;
@@ -225,11 +302,15 @@ __device__ __forceinline__ void refine_bucket(SelShared& sh, uint32_t need, int 
 }
 
 __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
-    const float* __restrict__ logits, int64_t stride, int V, int K, int cap,
-    float4* __restrict__ stats, int* __restrict__ counts, float* __restrict__ cand_x,
-    int* __restrict__ cand_i) {
+    const float* __restrict__ logits, int64_t stride, int V, int K, int cap, int q,
+    float4* __restrict__ stats, float* __restrict__ bounds, int* __restrict__ counts,
+    float* __restrict__ cand_x, int* __restrict__ cand_i) {
   __shared__ SelShared sh;
   __shared__ float red[3][4];
+  __shared__ float wbound[4][1 + kBounds];  // per wave: the chunk bound's and the r-bounds' parts
+  __shared__ float wmin[4][1];              // per wave: the quarter-form part of the chunk bound
+  __shared__ float stx[kMaxCap];            // candidates staged for coalesced stores
+  __shared__ int sti[kMaxCap];
   const int chunk = blockIdx.x, row = blockIdx.y, C = gridDim.x;
   const int base = chunk * kChunk;
   const int n = min(kChunk, V - base);
@@ -245,27 +326,113 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
   init_hists(sh);
   if (t == 0) sh.out_count = 0u;
 
-  float mx = -INFINITY;
+  float xmax = -INFINITY;  // the thread's largest value
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) mx = fmaxf(mx, x[j]);
-  mx = ddt::wave_reduce_uniform(mx, ddt::OpMax());
+  for (int j = 0; j < kPerThread; ++j) xmax = fmaxf(xmax, x[j]);
+  const float mx = ddt::wave_reduce_uniform(xmax, ddt::OpMax());
   if (lane == 0) red[0][wave] = mx;
-  __syncthreads();
+  lds_barrier();
   const float m = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
 
   float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    if (t + kChunkThreads * j < n) {
-      s += __expf(x[j] - m);
-      atomicAdd(&sh.hist[0][rel_digit(m, x[j])], 1u);  // pass 0
+  for (int j = 0; j < kPerThread; ++j)
+    if (t + kChunkThreads * j < n) s += __expf(x[j] - m);
+  s = ddt::wave_reduce_uniform(s, ddt::OpSum());
+
+  // Lower bounds without a histogram. Each thread takes the q-th largest of
+  // its 16 values (padding is -inf); sorted over the wave, the r-th largest
+  // of those, v_r, has r threads each holding q values >= v_r, so at least
+  // q r of the wave's (and the chunk's) values are >= v_r: v_r bounds the
+  // chunk's (q r)-th largest from below, and so does the maximum of the
+  // four waves' v_r. With q r >= Kc (r = ceil(Kc / q) <= 64) that bound T
+  // keeps every element of the chunk's top Kc in {x >= T}, usually not
+  // many more. The bounds for r = 1, 2, 4, ..., 64 go to the merge.
+  const uint32_t Kc = (uint32_t)min(K, n);
+  // Two forms of the bound for q r values: the maximum over the waves of
+  // their v_r (one wave holds them all), and the minimum over the waves of
+  // their v_(r/4) (each of the four waves holds a quarter), which is the
+  // tighter one whenever r >= 4.
+  {
+    const float sv = wave_sort_desc(qth_largest(x, q, xmax));
+    const int r_own = ((int)Kc + q - 1) / q;
+    const int r_quarter = (r_own + 3) / 4;
+    if (lane == 0) red[1][wave] = s;
+    const float own_max = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), r_own - 1));
+    const float own_min = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), r_quarter - 1));
+    if (lane == 0) {
+      wbound[wave][0] = own_max;
+      wmin[wave][0] = own_min;
+    }
+#pragma unroll
+    for (int b = 0; b < kBounds; ++b) {
+      const float vb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), (1 << b) - 1));
+      if (lane == 0) wbound[wave][1 + b] = vb;
     }
   }
-  s = ddt::wave_reduce_uniform(s, ddt::OpSum());
-  if (lane == 0) red[1][wave] = s;
-  __syncthreads();
+  lds_barrier();
+  const float T = fmaxf(fmaxf(fmaxf(wbound[0][0], wbound[1][0]), fmaxf(wbound[2][0], wbound[3][0])),
+                        fminf(fminf(wmin[0][0], wmin[1][0]), fminf(wmin[2][0], wmin[3][0])));
+  if (t < kBounds) {
+    // Bound b covers the chunk's (q 2^b)-th largest: one wave's v_(2^b), or
+    // for b >= 2 the four waves' v_(2^(b-2)).
+    float bb = fmaxf(fmaxf(wbound[0][1 + t], wbound[1][1 + t]), fmaxf(wbound[2][1 + t], wbound[3][1 + t]));
+    if (t >= 2)
+      bb = fmaxf(bb, fminf(fminf(wbound[0][t - 1], wbound[1][t - 1]),
+                           fminf(wbound[2][t - 1], wbound[3][t - 1])));
+    bounds[(int64_t)(row * C + chunk) * kBounds + t] = bb;
+  }
+  const int64_t slot0 = ((int64_t)row * C + chunk) * cap;
+  const float ssum = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  {
+    // Stage {x >= T} in LDS (positions by ballot, one LDS atomic per wave).
+    uint32_t wave_total = 0u;
+    uint32_t selmask = 0u;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const bool sel = t + kChunkThreads * j < n && x[j] >= T;
+      selmask |= (uint32_t)sel << j;
+      wave_total += (uint32_t)__popcll(ddt::ballot(sel));
+    }
+    uint32_t wbase = 0u;
+    if (lane == 0 && wave_total) wbase = atomicAdd(&sh.out_count, wave_total);
+    wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase);
+    uint32_t run = 0u;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const bool sel = (selmask >> j) & 1u;
+      const uint64_t bm = ddt::ballot(sel);
+      const uint32_t pos = wbase + run + ddt::lanes_below(bm);
+      if (sel && pos < (uint32_t)cap) {
+        stx[pos] = x[j];
+        sti[pos] = base + t + kChunkThreads * j;
+      }
+      run += (uint32_t)__popcll(bm);
+    }
+  }
+  lds_barrier();
+  const uint32_t n_fast = sh.out_count;
+  if (n_fast <= (uint32_t)cap) {
+    // The common case: every staged candidate goes out, coalesced.
+    for (uint32_t i = t; i < n_fast; i += kChunkThreads) {
+      cand_x[slot0 + i] = stx[i];
+      cand_i[slot0 + i] = sti[i];
+    }
+    if (t == 0) {
+      counts[row * C + chunk] = (int)n_fast;
+      stats[row * C + chunk] = make_float4(m, ssum, Kc == (uint32_t)K ? T : -INFINITY, 0.f);
+    }
+    return;
+  }
+  // Too many values at or above T (heavy ties or a flat chunk): select by
+  // radix instead, starting with the first digit's histogram.
+  lds_barrier();  // everyone has read out_count
+  if (t == 0) sh.out_count = 0u;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (t + kChunkThreads * j < n) atomicAdd(&sh.hist[0][rel_digit(m, x[j])], 1u);  // pass 0
+  lds_barrier();
 
-  const uint32_t Kc = (uint32_t)min(K, n);
   const DigitSel ds0 = find_digit(sh.hist[0], Kc);
   const uint32_t d0 = ds0.digit;
   const uint32_t need = ds0.need;
@@ -311,7 +478,6 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
   uint32_t wbase = 0u;
   if (lane == 0 && wave_total) wbase = atomicAdd(&sh.out_count, wave_total);
   wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase);
-  const int64_t slot0 = ((int64_t)row * C + chunk) * cap;
   uint32_t run = 0u;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
@@ -326,9 +492,8 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
   }
   tmin = ddt::wave_reduce_uniform(tmin, ddt::OpMin());
   if (lane == 0) red[2][wave] = tmin;
-  __syncthreads();
+  lds_barrier();
   if (t == 0) {
-    const float ssum = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
     const float tc = fminf(fminf(red[2][0], red[2][1]), fminf(red[2][2], red[2][3]));
     counts[row * C + chunk] = (int)sh.out_count;
     stats[row * C + chunk] = make_float4(m, ssum, Kc == (uint32_t)K ? tc : -INFINITY, 0.f);
@@ -338,43 +503,89 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
 struct MergeLds {
   SelShared sh;
   int offs[kMergeThreads + 1];  // exclusive prefix of chunk counts (C <= 1024)
+  int cnt[kMergeThreads];       // chunk counts
+  float taus[1 + kBounds];      // row thresholds from the chunks' r-bounds
   alignas(16) float sx[kSurvCap];
   alignas(16) int si[kSurvCap];
   alignas(16) float wx[DDTREE_MAX_K];
   alignas(16) int wi[DDTREE_MAX_K];
+  alignas(16) uint64_t rk[kMergeThreads];  // rank keys
+  int rkc[kMergeThreads / 4];              // ranks counted in parts
   float lse, tau, M;
-  int total;
+  int total, lg_slots;
   uint32_t nsurv, nkeep, nwin;
 };
 
-// Rank the n pairs in xs/is (n <= kMergeThreads, arrays padded to a multiple
-// of 16 with room) among themselves, one per thread, and write those ranked
-// below K. Starts with a barrier (after the pairs' writes).
-__device__ __forceinline__ void rank_and_write(float* xs, int* is, int n, int K, float lse,
+// The rank order as one unsigned 64-bit key: the logit's order key above,
+// the complement of the id below (among equal logits the smaller id ranks
+// first). Real keys are nonzero.
+__device__ __forceinline__ uint64_t rank_key(float x, int i) {
+  return ((uint64_t)ddt::f32_key(x) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+// Rank the n pairs in xs/is (n <= kMergeThreads) among themselves, one per
+// thread, and write those ranked below K. Each pair's key goes to keys[]
+// (padded with zeros, which beat nothing); a thread's rank is the number of
+// keys above its own, counted 8 at a time from 16-byte LDS reads. Starts
+// with a barrier (after the pairs' writes).
+// With n <= kMergeThreads / 4 the keys are counted in four quarters by four
+// threads per pair, whose counts meet in ranks[] (LDS atomics).
+__device__ __forceinline__ void rank_and_write(const float* xs, const int* is, uint64_t* keys,
+                                               int* ranks, int n, int K, float lse,
                                                float* out_lp, int32_t* out_tok) {
   const int t = threadIdx.x;
-  const int npad = (n + 15) & ~15;
-  __syncthreads();
-  if (t >= n && t < npad) {
-    xs[t] = -INFINITY;
-    is[t] = 0x7FFFFFFF;
-  }
-  __syncthreads();
+  constexpr int kParts = 4, kPartThreads = kMergeThreads / kParts;
+  const bool split = n <= kPartThreads;
+  const int npad = split ? (n + 8 * kParts - 1) & ~(8 * kParts - 1) : (n + 7) & ~7;
+  lds_barrier();
+  float xt = 0.f;
+  int it = 0;
+  uint64_t mine = 0;
   if (t < n) {
-    const float xt = xs[t];
-    const int it = is[t];
-    const int rank = rank_among(xs, is, npad, xt, it);
-    if (rank < K) {
+    xt = xs[t];
+    it = is[t];
+    mine = rank_key(xt, it);
+  }
+  if (t < npad) keys[t] = mine;
+  if (split && t < kPartThreads) ranks[t] = 0;
+  lds_barrier();
+  const int c = split ? t % kPartThreads : t;  // the pair this thread counts for
+  const int part = split ? t / kPartThreads : 0;
+  const int len = split ? npad / kParts : npad;
+  if (c < n) {
+    const uint64_t key = split ? keys[c] : mine;
+    int rank = 0;
+    for (int u = part * len; u < (part + 1) * len; u += 8) {
+      ulonglong2 a[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[k] = *reinterpret_cast<const ulonglong2*>(keys + u + 2 * k);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) rank += (int)(a[k].x > key) + (int)(a[k].y > key);
+    }
+    if (split) {
+      atomicAdd(&ranks[c], rank);
+    } else if (rank < K) {
       out_lp[rank] = xt - lse;
       out_tok[rank] = it;
+    }
+  }
+  if (split) {
+    lds_barrier();
+    if (t < n) {
+      const int rank = ranks[t];
+      if (rank < K) {
+        out_lp[rank] = xt - lse;
+        out_tok[rank] = it;
+      }
     }
   }
 }
 
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
-    int C, int K, int cap, int idx_passes, const float4* __restrict__ stats,
-    const int* __restrict__ counts, const float* __restrict__ cand_x,
-    const int* __restrict__ cand_i, float* __restrict__ logp, int32_t* __restrict__ token) {
+    int C, int K, int cap, int q, int idx_passes, const float4* __restrict__ stats,
+    const float* __restrict__ bounds, const int* __restrict__ counts,
+    const float* __restrict__ cand_x, const int* __restrict__ cand_i, float* __restrict__ logp,
+    int32_t* __restrict__ token) {
   __shared__ MergeLds s;
   const int row = blockIdx.x, t = threadIdx.x, lane = t & 63;
   const float4* st = stats + (int64_t)row * C;
@@ -382,7 +593,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   const float* cx = cand_x + (int64_t)row * C * cap;
   const int* ci = cand_i + (int64_t)row * C * cap;
 
-  // Chunk metadata: prefix offsets of the candidate lists, lse and tau.
+  // Chunk metadata: counts, lse and tau.
   if (t < 64) {
     // One chunk per lane per round; the first round's stats and counts
     // (C <= 64 in the common case) are loaded once and kept.
@@ -397,24 +608,17 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
       tau = fmaxf(tau, ddt::wave_reduce_uniform(v.z, ddt::OpMax()));
     }
     float S = 0.f;
-    int carry = 0;
+    int cmax = 1;
     for (int c0 = 0; c0 < C; c0 += 64) {
       const int c = c0 + lane;
       const float4 v = c0 == 0 ? v0 : (c < C ? st[c] : make_float4(-INFINITY, 0.f, -INFINITY, 0.f));
       S += ddt::wave_reduce_uniform(c < C ? v.y * expf(v.x - M) : 0.f, ddt::OpSum());
-      int x = c0 == 0 ? n0 : (c < C ? cnt[c] : 0);
-      int incl = x;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-      }
-      if (c < C) s.offs[c] = carry + incl - x;
-      carry += __shfl(incl, 63, 64);
+      const int x = c0 == 0 ? n0 : (c < C ? cnt[c] : 0);
+      if (c < C) s.cnt[c] = x;
+      cmax = max(cmax, (int)ddt::wave_reduce_uniform((float)x, ddt::OpMax()));
     }
     if (lane == 0) {
-      s.offs[C] = carry;
-      s.total = carry;
+      s.lg_slots = 32 - __builtin_clz((uint32_t)cmax - 1u | 1u);  // 2^lg >= every count
       s.M = M;
       s.tau = tau;
       s.lse = M + logf(S);
@@ -424,15 +628,34 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
       s.sh.out_count = 0u;
     }
   }
+  else if (t < 64 * (1 + kBounds)) {
+    // Wave b: chunk c holds at least q 2^(b-1) values >= its bound
+    // bounds[c][b - 1], so the need-th largest of those bounds over the
+    // chunks, need = ceil(K / (q 2^(b-1))), has at least K values of the
+    // row at or above it: a lower bound of the row's K-th largest.
+    const int b = (t >> 6) - 1;
+    const int per = q << b;
+    const int need = (K + per - 1) / per;
+    float tb = -INFINITY;
+    if (C <= 64 && need <= C) {
+      const float v = lane < C ? bounds[((int64_t)row * C + lane) * kBounds + b] : -INFINITY;
+      const float sv = wave_sort_desc(v);
+      tb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), need - 1));
+    }
+    if (lane == 0) s.taus[1 + b] = tb;
+  }
   init_hists(s.sh);
-  __syncthreads();
-  const int total = s.total;
-  const float tau = s.tau, M = s.M, lse = s.lse;
+  lds_barrier();
+  float tau_best = s.tau;
+#pragma unroll
+  for (int b = 0; b < kBounds; ++b) tau_best = fmaxf(tau_best, s.taus[1 + b]);
+  const float tau = tau_best, M = s.M, lse = s.lse;
   float* out_lp = logp + (int64_t)row * K;
   int32_t* out_tok = token + (int64_t)row * K;
 
   // Candidate i of the row (the chunks' lists concatenated): its chunk is
-  // found by binary search over the prefix offsets.
+  // found by binary search over the prefix offsets (made by make_offsets,
+  // only on the path that needs them).
   auto cand_at = [&](int i) -> int64_t {
     int lo = 0, hi = C;  // last chunk with offs[c] <= i
     while (hi - lo > 1) {
@@ -444,17 +667,23 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   // One pass over the candidates, kLoadBatch per thread at a time: keep(x)
   // says which to append to sx/si (one LDS atomic per wave on `counter`;
   // slots past kSurvCap are dropped, the counter still counts them).
+  // Slots: chunk c's list padded to 2^lg_slots entries (lg_slots covers
+  // the longest list), so a slot's chunk and position are a shift and a
+  // mask away.
+  const int lg = s.lg_slots;
+  const int nslots = C << lg;
   auto gather = [&](uint32_t* counter, auto keep) {
-    for (int g0 = 0; g0 < total; g0 += kMergeThreads * kLoadBatch) {
+    for (int g0 = 0; g0 < nslots; g0 += kMergeThreads * kLoadBatch) {
       float xv[kLoadBatch];
       int iv[kLoadBatch];
 #pragma unroll
       for (int r = 0; r < kLoadBatch; ++r) {
-        const int i = g0 + t + kMergeThreads * r;
+        const int g = g0 + t + kMergeThreads * r;
+        const int c = g >> lg, j = g & ((1 << lg) - 1);
         xv[r] = -INFINITY;
         iv[r] = -1;
-        if (i < total) {
-          const int64_t at = cand_at(i);
+        if (g < nslots && j < s.cnt[c]) {
+          const int64_t at = (int64_t)c * cap + j;
           xv[r] = cx[at];
           iv[r] = ci[at];
         }
@@ -478,17 +707,18 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   };
 
   // Survivors: the candidates >= tau (every top-K element is one), each also
-  // counted in the histogram of the first digit relative to the row max.
+  // counted in the histogram of the first digit relative to the row max
+  // (used when there are too many to rank all against all).
   gather(&s.nsurv, [&](float x) {
     const bool k = x >= tau;
     if (k) atomicAdd(&s.sh.hist[0][rel_digit(M, x)], 1u);
     return k;
   });
-  __syncthreads();
+  lds_barrier();
   int nsurv = (int)s.nsurv;
   if (nsurv <= kRankAllMax) {
     // Few survivors: rank each among all of them.
-    rank_and_write(s.sx, s.si, nsurv, K, lse, out_lp, out_tok);
+    rank_and_write(s.sx, s.si, s.rk, s.rkc, nsurv, K, lse, out_lp, out_tok);
     return;
   }
 
@@ -502,7 +732,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     // The survivors overflowed LDS (a large K): gather only bucket d0 and
     // above, in a second pass.
     gather(&s.nkeep, [&](float x) { return x >= tau && rel_digit(M, x) >= d0; });
-    __syncthreads();
+    lds_barrier();
     nsurv = (int)n_top;
     in_lds = true;
   }
@@ -517,7 +747,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
         s.wi[pos] = s.si[i];
       }
     }
-    rank_and_write(s.wx, s.wi, (int)n_top, K, lse, out_lp, out_tok);
+    rank_and_write(s.wx, s.wi, s.rk, s.rkc, (int)n_top, K, lse, out_lp, out_tok);
     return;
   }
 
@@ -525,6 +755,31 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   // radix select of the K largest inside bucket d0, over the survivors in
   // LDS, else over the candidates in global memory (those below tau are not
   // survivors there and are skipped), then rank the K winners.
+  int total = 0;
+  if (!in_lds) {
+    // Prefix offsets of the chunks' lists for cand_at (this path only).
+    if (t < 64) {
+      int carry = 0;
+      for (int c0 = 0; c0 < C; c0 += 64) {
+        const int c = c0 + lane;
+        const int x = c < C ? s.cnt[c] : 0;
+        int incl = x;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += o;
+        }
+        if (c < C) s.offs[c] = carry + incl - x;
+        carry += __shfl(incl, 63, 64);
+      }
+      if (lane == 0) {
+        s.offs[C] = carry;
+        s.total = carry;
+      }
+    }
+    lds_barrier();
+    total = s.total;
+  }
   const int n_all = in_lds ? nsurv : total;
   auto elem_x = [&](int i) -> float { return in_lds ? s.sx[i] : cx[cand_at(i)]; };
   auto elem_i = [&](int i) -> int { return in_lds ? s.si[i] : ci[cand_at(i)]; };
@@ -568,7 +823,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
       }
     }
   }
-  rank_and_write(s.wx, s.wi, K, K, lse, out_lp, out_tok);
+  rank_and_write(s.wx, s.wi, s.rk, s.rkc, K, K, lse, out_lp, out_tok);
 }
 
 }  // namespace
@@ -585,8 +840,11 @@ TopkPlan topk_plan(int L, int V, int K) {
   while (bits < 31 && ((int64_t)1 << bits) < (int64_t)V) ++bits;
   p.idx_passes = (bits + 7) / 8;
   const size_t LC = (size_t)L * p.C;
+  p.q = 1;
+  while (p.q < 16 && p.q * 64 < K) p.q <<= 1;
   p.stats_off = 0;
-  p.counts_off = align_up(p.stats_off + LC * sizeof(float4), 256);
+  p.bounds_off = align_up(p.stats_off + LC * sizeof(float4), 256);
+  p.counts_off = align_up(p.bounds_off + LC * kBounds * sizeof(float), 256);
   p.candx_off = align_up(p.counts_off + LC * sizeof(int), 256);
   p.candi_off = align_up(p.candx_off + LC * p.cap * sizeof(float), 256);
   p.bytes = align_up(p.candi_off + LC * p.cap * sizeof(int), 256);
@@ -599,15 +857,16 @@ int topk_launch(const float* logits, int64_t stride, int L, int V, int K,
   if (p.C > kMergeThreads) return DDTREE_ERR_UNSUPPORTED;
   char* w = static_cast<char*>(ws);
   float4* stats = reinterpret_cast<float4*>(w + p.stats_off);
+  float* bounds = reinterpret_cast<float*>(w + p.bounds_off);
   int* counts = reinterpret_cast<int*>(w + p.counts_off);
   float* cx = reinterpret_cast<float*>(w + p.candx_off);
   int* ci = reinterpret_cast<int*>(w + p.candi_off);
   hipLaunchKernelGGL(topk_chunk_kernel, dim3(p.C, L), dim3(kChunkThreads), 0, stream,
-                     logits, stride, V, K, p.cap, stats, counts, cx, ci);
+                     logits, stride, V, K, p.cap, p.q, stats, bounds, counts, cx, ci);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return launch_status(e);
   hipLaunchKernelGGL(topk_merge_kernel, dim3(L), dim3(kMergeThreads), 0, stream,
-                     p.C, K, p.cap, p.idx_passes, stats, counts, cx, ci, logp, token);
+                     p.C, K, p.cap, p.q, p.idx_passes, stats, bounds, counts, cx, ci, logp, token);
   return launch_status(hipGetLastError());
 }
 

@@ -97,3 +97,36 @@ def test_wide_spread_logits():
     ref, _ = st.topk(x, 700)
     tol = 4 * float(np.spacing(np.float32(np.abs(ref).max())))
     _check(x, 700, lp_atol=tol)
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 16, 63, 64, 65, 128, 129, 256, 257, 512, 1000, 1024])
+def test_bounds_every_k(K):
+    """Each K takes its own per-thread order statistic q (1, 2, 4, 8, 16) and
+    wave ranks r for the chunk bound and for the merge's row threshold; four
+    rows of the peaked and of the confident drafter families."""
+    xs = [synth.drafter_logits(synth.WORKLOADS[name]).x[:2] for name in ("coder30b_b64", "sweep_b16")]
+    _check(np.concatenate(xs), K, twice=False)
+
+
+@pytest.mark.parametrize("K", [16, 64, 200, 1024])
+def test_bounds_top_values_bunched(K):
+    """The largest values of every 4096-logit chunk sit in the 16-value slices
+    of the fewest threads that can hold them (row 0), in the lanes of one wave
+    (row 1), or as exact ties in a few threads (row 2): the per-thread and
+    per-wave order statistics behind the bounds see them bunched together."""
+    g = synth.rng("test", 505, K)
+    L, V = 3, 40000
+    x = g.standard_normal((L, V)).astype(np.float32)
+    nthreads = -(-K // 16)
+    for base in range(0, V, 4096):
+        n = min(4096, V - base)
+        for t in range(nthreads):
+            pos = base + t + 256 * np.arange(16)
+            pos = pos[pos < base + n]
+            x[0, pos] = 10.0 + g.standard_normal(pos.size).astype(np.float32)
+            x[2, pos] = 10.0
+        steps = -(-K // 64)
+        pos = base + 128 + np.arange(64)[None, :] + 256 * np.arange(steps)[:, None]
+        pos = pos[pos < base + n]
+        x[1, pos] = 10.0 + g.standard_normal(pos.size).astype(np.float32)
+    _check(x, K)
