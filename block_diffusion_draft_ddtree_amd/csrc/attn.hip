@@ -134,6 +134,25 @@ __device__ __forceinline__ float halves_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// n / d and n mod d for 0 <= n < 2^31, d >= 1 and a quotient below 2^22
+// (every use here divides an index by a count it indexes), without the
+// integer division routine: the float estimate n * (1 / d) carries a
+// relative error below 2^-22 (the reciprocal, the conversion of n and the
+// product each round once), so it is within one of the quotient, and one
+// comparison of the remainder corrects it.
+struct Div {
+  int d;
+  float rcp;
+  __device__ __forceinline__ explicit Div(int d_) : d(d_), rcp(__builtin_amdgcn_rcpf((float)d_)) {}
+  __device__ __forceinline__ int quot(int n) const {
+    int q = (int)((float)n * rcp);
+    const int r = n - q * d;
+    q += r < 0 ? -1 : (r >= d ? 1 : 0);
+    return q;
+  }
+  __device__ __forceinline__ int rem(int n, int q) const { return n - q * d; }
+};
+
 // Per-lane source offsets of a wave's copies, fixed for the whole kernel:
 // copy i of row wave rw fetches rows 4 (rw * COPIES + i) + lane / NS (D =
 // 128), each lane the chunk that belongs at its 16-byte slot.
@@ -463,11 +482,14 @@ __device__ __forceinline__ void attn_workgroup(
   __shared__ float2 mlx[kWaves * 64];
   __shared__ uint32_t mrows[kRowsPerTile * kMaxMaskWords];
 
-  const int tile = idx % tiles;
-  const int gs = idx / tiles;
-  const int split = gs % splits, g = gs / splits;
+  const Div div_tiles(tiles), div_splits(splits);
+  const int gs = div_tiles.quot(idx);
+  const int tile = div_tiles.rem(idx, gs);
+  const int g = div_splits.quot(gs);
+  const int split = div_splits.rem(gs, g);
 
-  const int G = Hq / Hkv, R = N * G;
+  const Div div_G(Div(Hkv).quot(Hq));
+  const int G = div_G.d, R = N * G;
   // The wave index is uniform: keep it (and all that derives from it, such
   // as the LDS destinations of the copies) in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -478,8 +500,9 @@ __device__ __forceinline__ void attn_workgroup(
   const bool live = row0 < R;  // wave-uniform: the wave has query rows
   const int rho = row0 + j;
   const bool row_ok = rho < R;
-  const int node = row_ok ? rho / G : 0;
-  const int hq = g * G + (row_ok ? rho % G : 0);
+  const int rho_n = div_G.quot(rho);
+  const int node = row_ok ? rho_n : 0;
+  const int hq = g * G + (row_ok ? div_G.rem(rho, rho_n) : 0);
 
   const int KT = S + N;
   const int NSB = (KT + kSBK - 1) / kSBK;
@@ -492,7 +515,7 @@ __device__ __forceinline__ void attn_workgroup(
   // superblocks at first and later find most lines in the XCD's L2. The
   // online softmax does not depend on the key order.
   const int nsb = sb1 - sb0;
-  const int rot = tile % nsb;
+  const int rot = tile - Div(nsb).quot(tile) * nsb;
   auto sb_at = [&](int i) {
     const int r = i + rot;
     return sb0 + (r < nsb ? r : r - nsb);
@@ -524,7 +547,8 @@ __device__ __forceinline__ void attn_workgroup(
       const int copy = st * QC + i;
       const int row = copy * C::ROWS_PER_COPY + lane / C::NS;
       const int rr = min(row0 + row, R - 1);
-      const int qrow = (rr / G) * Hq + g * G + rr % G;
+      const int rn = div_G.quot(rr);
+      const int qrow = rn * Hq + g * G + div_G.rem(rr, rn);
       const char* src = reinterpret_cast<const char*>(q + (int64_t)qrow * D) +
                         16 * ((lane % C::NS) ^ fk<D>(row));
       __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(qdst + copy * 1024), 16, 0, 0);
@@ -538,10 +562,11 @@ __device__ __forceinline__ void attn_workgroup(
   const int Wn = (N + 31) >> 5;
   const int tile_row0 = tile * kRowsPerTile;
   if (sb1 * kSBK > S) {
+    const Div div_Wn(Wn);
     for (int i = threadIdx.x; i < kRowsPerTile * Wn; i += kThreads) {
-      const int r = i / Wn, w = i - r * Wn;
+      const int r = div_Wn.quot(i), w = div_Wn.rem(i, r);
       const int rr = min(tile_row0 + r, R - 1);
-      mrows[i] = anc[(int64_t)(rr / G) * W + w];
+      mrows[i] = anc[(int64_t)div_G.quot(rr) * W + w];
     }
   }
   // A pruned tree (ddtree_tree_prune) has empty ancestor rows for the nodes
@@ -550,8 +575,8 @@ __device__ __forceinline__ void attn_workgroup(
   // everything has landed (below).
   uint32_t own = 0u;
   {
-    const int n_first = tile_row0 / G;
-    const int n_last = min(R - 1, tile_row0 + kRowsPerTile - 1) / G;
+    const int n_first = div_G.quot(tile_row0);
+    const int n_last = div_G.quot(min(R - 1, tile_row0 + kRowsPerTile - 1));
     const int n = n_first + lane;  // at most 64 nodes per tile
     if (n <= n_last) own = (anc[(int64_t)n * W + (n >> 5)] >> (n & 31)) & 1u;
   }
@@ -797,8 +822,11 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
   const int wbl = t / (256 * DT);  // (kv-head, tile, row wave)
   const int WB = Hkv * tiles * kRowWaves;
   if (wbl >= WB) return;
-  const int rw = wbl % kRowWaves, tile = (wbl / kRowWaves) % tiles, g = wbl / (kRowWaves * tiles);
-  const int G = Hq / Hkv, R = N * G;
+  const int rw = wbl % kRowWaves;
+  const Div div_tiles(tiles), div_G(Div(Hkv).quot(Hq));
+  const int g = div_tiles.quot(wbl / kRowWaves);
+  const int tile = div_tiles.rem(wbl / kRowWaves, g);
+  const int G = div_G.d, R = N * G;
   const int j = lane & 31, h = lane >> 5;
   const int rho = tile * kRowsPerTile + rw * 32 + j;
   if (rho >= R) return;
@@ -806,7 +834,7 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
   // have run) and no output. The check's load goes out with the partials'
   // loads and is tested before the store (a dropped row merges whatever the
   // workspace holds and discards it), so it adds no round trip.
-  const int node = rho / G;
+  const int node = div_G.quot(rho);
   const uint32_t own_word = anc[(int64_t)node * W + (node >> 5)];
   const uint2* po = reinterpret_cast<const uint2*>(part_o);
   const float2* pml = reinterpret_cast<const float2*>(part_ml);
@@ -848,7 +876,7 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
   }
   if (!((own_word >> (node & 31)) & 1u)) return;
   const float inv = 1.0f / L;
-  const int hq = g * G + rho % G;
+  const int hq = g * G + div_G.rem(rho, node);
   const int d0 = 32 * dt + 8 * qd + 4 * h;
   uint2 pk;
   pk.x = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
