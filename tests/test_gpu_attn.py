@@ -203,3 +203,30 @@ def test_max_nodes_d64_full():
     q_bits, q, kv_bits, kv, g = _inputs(1025, 4, 1, 64, 300, 6)
     anc = _tree_anc("random", 1025, g)
     _run(q_bits, q, kv_bits, kv, 300, anc)
+
+
+def test_large_values_through_split_partials():
+    """The split path stores each split's normalised output as fp16, whose
+    range ends at 65504 (the documented limit on |V|): V at magnitudes up to
+    2^15 (bf16-exact) at the 30B shape, where the key range runs as 7
+    splits. Every element compared after dividing both sides by V's scale
+    (the tolerance is stated for unit-scale values), so an overflow or a
+    lost split shows."""
+    N, Hq, Hkv, D, S = 65, 32, 4, 128, 4096
+    q_bits, q, kv_bits, kv, g = _inputs(N, Hq, Hkv, D, S, 12)
+    big = np.float32(2.0 ** 14)
+    kv = kv.copy()
+    kv[1] = np.clip(kv[1] * big, -2.0 * big, 2.0 * big)
+    kv_bits = synth.f32_to_bf16_bits(kv)
+    kv = synth.bf16_bits_to_f32(kv_bits)
+    parent = [-1] + [int(g.integers(max(0, n - 4), n)) for n in range(1, N)]
+    anc = ot.ancestor_mask(parent)
+    assert bd.ddtree_tree_attn_workspace_bytes(N, Hq, Hkv, D, S) > 0  # the split path
+    say(f"attn large V N={N} S={S}")
+    kvd = up_bf16(kv_bits)
+    out = bd.ddtree_tree_attn(up_bf16(q_bits), kvd[0], kvd[1], S, up(anc.view(np.int32)), 0.25)
+    got = down_bf16_f32(out)
+    assert np.isfinite(got).all()
+    ref = oa.tree_attention(q, kv[0], kv[1], S, anc, 0.25)
+    assert np.abs(ref).max() > 1000.0  # the outputs do reach the large scale
+    assert_attn_close(got / big, ref / big, "large V through the split path")
