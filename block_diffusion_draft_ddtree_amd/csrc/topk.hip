@@ -23,6 +23,8 @@
 // for exact ties, on the index (smaller id first). The chunk kernel stops
 // after the first digit when the candidate set fits its slots ("loose").
 // Ranking is by (logit descending, token id ascending) throughout.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace {
@@ -33,7 +35,8 @@ constexpr int kChunk = kChunkThreads * kPerThread;  // 4096
 constexpr int kLooseExtra = 256;                     // slots beyond K per chunk
 constexpr int kMergeThreads = 1024;
 constexpr int kSurvCap = 16384;                      // survivors selected in LDS (128 KB)
-constexpr int kLoadBatch = 8;                        // candidates loaded per thread at once
+constexpr int kLoadBatchSmall = 8;                   // candidates loaded per thread at once:
+constexpr int kLoadBatchLarge = 16;                  // the small batch when it holds all
 constexpr int kRankAllMax = 256;                     // survivors ranked all against all
 constexpr int kBounds = 7;                           // per-chunk bounds: r = 1, 2, 4, ..., 64
 constexpr int kMaxCap = DDTREE_MAX_K + kLooseExtra;  // candidate slots per chunk
@@ -512,7 +515,7 @@ struct MergeLds {
   alignas(16) uint64_t rk[kMergeThreads];  // rank keys
   int rkc[kMergeThreads / 4];              // ranks counted in parts
   float lse, tau, M;
-  int total, lg_slots;
+  int total, slots_per;
   uint32_t nsurv, nkeep, nwin;
 };
 
@@ -618,7 +621,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
       cmax = max(cmax, (int)ddt::wave_reduce_uniform((float)x, ddt::OpMax()));
     }
     if (lane == 0) {
-      s.lg_slots = 32 - __builtin_clz((uint32_t)cmax - 1u | 1u);  // 2^lg >= every count
+      s.slots_per = cmax;  // the longest list
       s.M = M;
       s.tau = tau;
       s.lse = M + logf(S);
@@ -664,43 +667,69 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     }
     return (int64_t)lo * cap + (i - s.offs[lo]);
   };
-  // One pass over the candidates, kLoadBatch per thread at a time: keep(x)
-  // says which to append to sx/si (one LDS atomic per wave on `counter`;
-  // slots past kSurvCap are dropped, the counter still counts them).
-  // Slots: chunk c's list padded to 2^lg_slots entries (lg_slots covers
-  // the longest list), so a slot's chunk and position are a shift and a
-  // mask away.
-  const int lg = s.lg_slots;
-  const int nslots = C << lg;
-  auto gather = [&](uint32_t* counter, auto keep) {
-    for (int g0 = 0; g0 < nslots; g0 += kMergeThreads * kLoadBatch) {
-      float xv[kLoadBatch];
-      int iv[kLoadBatch];
+  // One pass over the candidates: keep(x) says which to append to sx/si
+  // (slots past kSurvCap are dropped, the counter still counts them).
+  // Chunk c's list is read by the tpc = floor(1024 / C) threads
+  // [c tpc, (c + 1) tpc), thread u of them taking positions u, u + tpc,
+  // u + 2 tpc, ...: a thread reads its chunk's count once and then issues
+  // all its loads (one pass of NB per thread; one pass at K = 64 on the
+  // full vocabulary, 38 chunks x <= 137) before using any. NB is 8 when
+  // that covers the longest list, else 16: the gather's code is unrolled
+  // over NB, and a one-pass kernel pays for every instruction it fetches,
+  // so the short form is the faster one wherever it suffices. A thread's kept
+  // values go out in one run: an exclusive prefix of the per-thread counts
+  // over the wave (five ballots of their bits) and one LDS atomic per wave.
+  const int tpc = kMergeThreads / C;
+  const int my_c = t / tpc;
+  const int my_u = t - my_c * tpc;
+  const int my_n = my_c < C ? s.cnt[my_c] : 0;
+  const int per_thread = (s.slots_per + tpc - 1) / tpc;
+  const float* my_cx = cx + (int64_t)min(my_c, C - 1) * cap;
+  const int* my_ci = ci + (int64_t)min(my_c, C - 1) * cap;
+  static_assert(kLoadBatchLarge <= 31, "per-thread counts fit five bits");
+  auto gather_nb = [&](auto nb_const, uint32_t* counter, auto keep) {
+    constexpr int NB = decltype(nb_const)::value;
+    for (int r0 = 0; r0 < per_thread; r0 += NB) {
+      float xv[NB];
+      int iv[NB];
 #pragma unroll
-      for (int r = 0; r < kLoadBatch; ++r) {
-        const int g = g0 + t + kMergeThreads * r;
-        const int c = g >> lg, j = g & ((1 << lg) - 1);
+      for (int r = 0; r < NB; ++r) {
+        const int jj = my_u + tpc * (r0 + r);
         xv[r] = -INFINITY;
         iv[r] = -1;
-        if (g < nslots && j < s.cnt[c]) {
-          const int64_t at = (int64_t)c * cap + j;
-          xv[r] = cx[at];
-          iv[r] = ci[at];
+        if (r0 + r >= per_thread) continue;  // uniform
+        if (jj < my_n) {
+          xv[r] = my_cx[jj];
+          iv[r] = my_ci[jj];
         }
       }
+      uint32_t km = 0u, nk = 0u;
 #pragma unroll
-      for (int r = 0; r < kLoadBatch; ++r) {
+      for (int r = 0; r < NB; ++r) {
+        if (r0 + r >= per_thread) continue;  // uniform
         const bool k = iv[r] >= 0 && keep(xv[r]);
-        const uint64_t bm = ddt::ballot(k);
-        uint32_t wb = 0u;
-        if (lane == 0 && bm) wb = atomicAdd(counter, (uint32_t)__popcll(bm));
-        wb = (uint32_t)__builtin_amdgcn_readfirstlane((int)wb);
-        if (k) {
-          const uint32_t pos = wb + ddt::lanes_below(bm);
+        km |= (uint32_t)k << r;
+        nk += (uint32_t)k;
+      }
+      uint32_t excl = 0u, tot = 0u;
+#pragma unroll
+      for (int b = 0; b < 5; ++b) {
+        const uint64_t bm = ddt::ballot((nk >> b) & 1u);
+        excl += ddt::lanes_below(bm) << b;
+        tot += (uint32_t)__popcll(bm) << b;
+      }
+      uint32_t wb = 0u;
+      if (lane == 0 && tot) wb = atomicAdd(counter, tot);
+      uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane((int)wb) + excl;
+#pragma unroll
+      for (int r = 0; r < NB; ++r) {
+        if (r0 + r >= per_thread) continue;  // uniform
+        if ((km >> r) & 1u) {
           if (pos < (uint32_t)kSurvCap) {
             s.sx[pos] = xv[r];
             s.si[pos] = iv[r];
           }
+          ++pos;
         }
       }
     }
@@ -709,6 +738,12 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   // Survivors: the candidates >= tau (every top-K element is one), each also
   // counted in the histogram of the first digit relative to the row max
   // (used when there are too many to rank all against all).
+  auto gather = [&](uint32_t* counter, auto keep) {
+    if (per_thread <= kLoadBatchSmall)
+      gather_nb(std::integral_constant<int, kLoadBatchSmall>{}, counter, keep);
+    else
+      gather_nb(std::integral_constant<int, kLoadBatchLarge>{}, counter, keep);
+  };
   gather(&s.nsurv, [&](float x) {
     const bool k = x >= tau;
     if (k) atomicAdd(&s.sh.hist[0][rel_digit(M, x)], 1u);
