@@ -674,9 +674,9 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   // u + 2 tpc, ...: a thread reads its chunk's count once and then issues
   // all its loads (one pass of NB per thread; one pass at K = 64 on the
   // full vocabulary, 38 chunks x <= 137) before using any. NB is 8 when
-  // that covers the longest list, else 16: the gather's code is unrolled
-  // over NB, and a one-pass kernel pays for every instruction it fetches,
-  // so the short form is the faster one wherever it suffices. A thread's kept
+  // that covers the longest list, else 16 (measured: the 16-wide form is
+  // slower at small K although its extra iterations are skipped by uniform
+  // branches, and faster at large K, where it saves passes). A thread's kept
   // values go out in one run: an exclusive prefix of the per-thread counts
   // over the wave (five ballots of their bits) and one LDS atomic per wave.
   const int tpc = kMergeThreads / C;
