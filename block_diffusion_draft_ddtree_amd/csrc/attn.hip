@@ -4,12 +4,15 @@
 //
 // Decomposition. For kv-head g the query rows are rho = n * G + i (node n,
 // i-th query head of the group); all N * G rows share the same keys. A
-// workgroup owns a tile of 64 query rows (two waves of 32 rows) and a range
-// of keys, and runs four key streams side by side: the range is cut into
-// 128-key superblocks, and stream s computes the 32-key block s of every
-// superblock. So a workgroup is 8 waves (2 row waves x 4 streams), two per
-// SIMD: while one wave of a SIMD runs its softmax the other keeps the
-// matrix core busy. After the loop the four streams' partial results are
+// workgroup owns a tile of query rows (RW waves of 32 rows) and a range of
+// keys, and runs 8 / RW key streams side by side: the range is cut into
+// superblocks of 32 keys per stream, and stream s computes the 32-key
+// block s of every superblock. So a workgroup is 8 waves, two per SIMD:
+// while one wave of a SIMD runs its softmax the other keeps the matrix
+// core busy. RW = 2 (64-row tiles, 4 streams) below 1024 query rows per
+// kv-head, RW = 4 (128-row tiles, 2 streams) from there on, where each K/V
+// byte copied into LDS then serves twice the rows and there are tiles
+// enough to fill the chip. After the loop the streams' partial results are
 // merged through LDS. Blocks before S are dense prefix keys; only blocks
 // reaching past S read the ancestor mask.
 //
@@ -70,16 +73,27 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 constexpr int kBK = 32;                       // keys per block (one stream's step)
-constexpr int kStreams = 4;                   // key streams per workgroup
-constexpr int kRowWaves = 2;                  // 32-row query waves per workgroup
-constexpr int kWaves = kStreams * kRowWaves;  // 8: two per SIMD
+constexpr int kWaves = 8;                     // waves per workgroup: two per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerTile = 32 * kRowWaves;
-constexpr int kSBK = kBK * kStreams;          // keys per superblock
 constexpr int kXcds = 8;
 constexpr int kMaxMaskWords = (DDTREE_MAX_B + 1 + 31) / 32;  // words of an ancestor row
+// Query rows per kv-head (N * G) from which the tall tile shape is used.
+constexpr int kTallRows = 1024;
 
-template <int D>
+// Tile shape: RW 32-row query waves x 8 / RW key streams. RW = 2 (64-row
+// tiles, 4 streams, 128-key superblocks) for small trees; RW = 4 (128-row
+// tiles, 2 streams, 64-key superblocks) from kTallRows rows per kv-head on,
+// where each K/V byte copied into LDS then feeds twice the rows.
+template <int RW>
+struct Shape {
+  static_assert(RW == 2 || RW == 4, "row waves");
+  static constexpr int kRowWaves = RW;
+  static constexpr int kStreams = kWaves / RW;
+  static constexpr int kRowsPerTile = 32 * RW;
+  static constexpr int kSBK = kBK * kStreams;  // keys per superblock
+};
+
+template <int D, int RW = 2>
 struct Cfg {
   static constexpr int KS = D / 16;                          // MFMA k-steps for Q.K
   static constexpr int DT = D / 32;                          // 32-wide output tiles of P.V
@@ -87,9 +101,8 @@ struct Cfg {
   static constexpr int ROWB = 2 * D;                         // bytes per row
   static constexpr int TILEB = kBK * ROWB;                   // bytes per K or V block
   static constexpr int ROWS_PER_COPY = 1024 / ROWB;          // rows per 1 KB wave copy
-  static constexpr int COPIES = TILEB / 1024 / kRowWaves;    // copies per wave per block
-  static constexpr int STAGEB = kStreams * TILEB;            // one operand of a superblock
-  static constexpr int OB = 64 * DT * 16 * 4;                // one wave's fp32 output tile
+  static constexpr int COPIES = TILEB / 1024 / RW;           // copies per wave per block
+  static constexpr int STAGEB = Shape<RW>::kStreams * TILEB;  // one operand of a superblock
 };
 
 // K rows are read 32 at a time at one chunk: spread consecutive rows over
@@ -158,28 +171,28 @@ struct Div {
 // 128), each lane the chunk that belongs at its 16-byte slot.
 // (fv(row) depends only on the row modulo 4, i.e. on the lane, so the V
 // offsets of the copies differ by whole rows.)
-template <int D>
+template <int D, int RW>
 struct CopyLanes {
-  uint32_t kb[Cfg<D>::COPIES];  // byte offsets from the block's row 0
-  uint32_t vb;                  // V offset of copy 0; copy i adds i rows per copy
+  uint32_t kb[Cfg<D, RW>::COPIES];  // byte offsets from the block's row 0
+  uint32_t vb;                      // V offset of copy 0; copy i adds i rows per copy
 };
-template <int D>
+template <int D, int RW>
 __device__ __forceinline__ int copy_row(int rw, int i, int lane) {
-  using C = Cfg<D>;
+  using C = Cfg<D, RW>;
   return (rw * C::COPIES + i) * C::ROWS_PER_COPY + lane / C::NS;
 }
-template <int D>
-__device__ __forceinline__ CopyLanes<D> copy_lanes(int rw, int lane) {
-  using C = Cfg<D>;
+template <int D, int RW>
+__device__ __forceinline__ CopyLanes<D, RW> copy_lanes(int rw, int lane) {
+  using C = Cfg<D, RW>;
   static_assert(C::ROWS_PER_COPY % 4 == 0, "fv is periodic in 4 rows");
-  CopyLanes<D> cl;
+  CopyLanes<D, RW> cl;
   const int slot = lane % C::NS;
 #pragma unroll
   for (int i = 0; i < C::COPIES; ++i) {
-    const int row = copy_row<D>(rw, i, lane);
+    const int row = copy_row<D, RW>(rw, i, lane);
     cl.kb[i] = (uint32_t)(row * C::ROWB + 16 * (slot ^ fk<D>(row)));
   }
-  const int row0 = copy_row<D>(rw, 0, lane);
+  const int row0 = copy_row<D, RW>(rw, 0, lane);
   cl.vb = (uint32_t)(row0 * C::ROWB + 16 * (slot ^ fv<D>(row0)));
   return cl;
 }
@@ -209,13 +222,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* src
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, nrec, kRsrcWord3);
 }
 
-// Copy i of this row wave's share of a K or V block into LDS (the two row
+// Copy i of this row wave's share of a K or V block into LDS (the RW row
 // waves of a stream split a block's copies): 1 KB, lane l to +16 l, each
 // lane the chunk that belongs at its slot.
-template <int D, bool IS_V>
+template <int D, int RW, bool IS_V>
 __device__ __forceinline__ void copy_part(__amdgpu_buffer_rsrc_t rs, char* dst_lds, int rw,
-                                          const CopyLanes<D>& cl, int i) {
-  using C = Cfg<D>;
+                                          const CopyLanes<D, RW>& cl, int i) {
+  using C = Cfg<D, RW>;
   const uint32_t off = IS_V ? cl.vb + (uint32_t)(i * C::ROWS_PER_COPY * C::ROWB) : cl.kb[i];
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       rs, (lds_void_t*)(dst_lds + (rw * C::COPIES + i) * 1024), 16, off, 0, 0, 0);
@@ -326,10 +339,10 @@ __device__ __forceinline__ void block_pv(const char* Vb, const VLanes<D>& vl, co
 // chain of products, with the K operand reads kept a few steps ahead and
 // the copies kcopy(0 .. COPIES - 1) (of the next block, into the other
 // stage) placed between the last products.
-template <int D, class KCopy>
+template <int D, int RW, class KCopy>
 __device__ __forceinline__ f32x16 block_qk(const char* Kb, const bf16x8 (&qf)[Cfg<D>::KS],
                                            int lane, KCopy kcopy) {
-  using C = Cfg<D>;
+  using C = Cfg<D, RW>;
   const int j = lane & 31, h = lane >> 5;
   const char* krow = Kb + j * C::ROWB;
   const int f = fk<D>(j);
@@ -375,13 +388,13 @@ __device__ __forceinline__ f32x16 block_qk(const char* Kb, const bf16x8 (&qf)[Cf
 // a wave-uniform branch that touches only the scores. The copies
 // vcopy(0 .. COPIES - 1) (this block's V, into the stage the next step
 // reads) go between the products when PV, else after the score reduction.
-template <int D, bool PV, class VCopy>
+template <int D, int RW, bool PV, class VCopy>
 __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
                                                  const VLanes<D>& vl, PBlock& pb,
                                                  f32x16 (&o)[Cfg<D>::DT], float& m_run,
                                                  f32x16& lsum, float c, int lane, bool masked,
                                                  uint32_t vis, VCopy vcopy) {
-  using C = Cfg<D>;
+  using C = Cfg<D, RW>;
   const int h = lane >> 5;
   bf16x8 va[2][C::DT];
   if (PV) read_v<D>(Vprev, vl, va);
@@ -455,22 +468,28 @@ __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
 
 // Splits of a request's key range and its first split in the partials,
 // from its prefix length and the end of the previous request's workgroups.
+template <int RW>
 __device__ __forceinline__ int req_splits(int S, int N, int sb_per_split) {
-  return ((S + N + kSBK - 1) / kSBK + sb_per_split - 1) / sb_per_split;
+  constexpr int SBK = Shape<RW>::kSBK;
+  return ((S + N + SBK - 1) / SBK + sb_per_split - 1) / sb_per_split;
 }
 
 // The work of one workgroup: position idx in its request's (kv-head, split,
 // tile) order; q, k, v, anc and out already point at the request's slices;
 // part_base = the request's first split times Hkv (its partial tiles start
-// at part_base * tiles * kRowWaves).
-template <int D>
+// at part_base * tiles * RW).
+template <int D, int RW>
 __device__ __forceinline__ void attn_workgroup(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int S, int S_cap, int N, int Hq, int Hkv, float scale_log2,
     const uint32_t* __restrict__ anc, int W, uint16_t* __restrict__ out,
     float* __restrict__ part_o, float* __restrict__ part_ml, int tiles, int splits,
     int part_base, int sb_per_split, int idx) {
-  using C = Cfg<D>;
+  using C = Cfg<D, RW>;
+  constexpr int kRowWaves = Shape<RW>::kRowWaves;
+  constexpr int kStreams = Shape<RW>::kStreams;
+  constexpr int kRowsPerTile = Shape<RW>::kRowsPerTile;
+  constexpr int kSBK = Shape<RW>::kSBK;
   // Two stages per operand, as distinct arrays: every read and every copy
   // below names a fixed array, so the compiler can tell that reading one
   // stage never has to wait for the copy in flight into the other. Stream s
@@ -479,6 +498,11 @@ __device__ __forceinline__ void attn_workgroup(
   __shared__ __attribute__((aligned(1024))) char v0[C::STAGEB];
   __shared__ __attribute__((aligned(1024))) char k1[C::STAGEB];
   __shared__ __attribute__((aligned(1024))) char v1[C::STAGEB];
+  // Q of the tile: with 4 streams it fits the second K stage (free until
+  // step 0 copies into it); with 2 it needs an array of its own.
+  constexpr bool kQInK1 = kRowWaves * C::TILEB <= C::STAGEB;
+  __shared__ __attribute__((aligned(1024))) char qown[kQInK1 ? 16 : kRowWaves * C::TILEB];
+  char* const qs = kQInK1 ? k1 : qown;
   __shared__ float2 mlx[kWaves * 64];
   __shared__ uint32_t mrows[kRowsPerTile * kMaxMaskWords];
 
@@ -494,7 +518,7 @@ __device__ __forceinline__ void attn_workgroup(
   // as the LDS destinations of the copies) in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int st = wave >> 1, rw = wave & 1;
+  const int st = wave / kRowWaves, rw = wave % kRowWaves;
   const int j = lane & 31, h = lane >> 5;
   const int row0 = tile * kRowsPerTile + rw * 32;
   const bool live = row0 < R;  // wave-uniform: the wave has query rows
@@ -524,7 +548,7 @@ __device__ __forceinline__ void attn_workgroup(
   const uint16_t* vh = v + (int64_t)g * S_cap * D;
   const int soff = st * C::TILEB;
 
-  const CopyLanes<D> cl = copy_lanes<D>(rw, lane);
+  const CopyLanes<D, RW> cl = copy_lanes<D, RW>(rw, lane);
   // Blocks wholly past the last key are still copied (as zero rows) and
   // computed (every key masked): every wave then runs one straight path,
   // and no stage ever holds data that is not finite.
@@ -532,16 +556,16 @@ __device__ __forceinline__ void attn_workgroup(
   {
     const auto rk = block_rsrc<D>(kh, (sb_at(0) * kStreams + st) * kBK, KT, true);
 #pragma unroll
-    for (int i = 0; i < C::COPIES; ++i) copy_part<D, false>(rk, k0 + soff, rw, cl, i);
+    for (int i = 0; i < C::COPIES; ++i) copy_part<D, RW, false>(rk, k0 + soff, rw, cl, i);
   }
   // Q of the tile goes through LDS too: the 32 rows of row wave rw land in
-  // k1 (free until step 0 copies into it) laid out like a K block, copied
-  // by that row wave's four stream waves with whole-row coalesced reads
-  // (lanes holding Q^T operands would each touch a different row). Rows
-  // past R are clamped to row R - 1: finite data whose results are dropped.
+  // qs laid out like a K block, copied by that row wave's stream waves with
+  // whole-row coalesced reads (lanes holding Q^T operands would each touch
+  // a different row). Rows past R are clamped to row R - 1: finite data
+  // whose results are dropped.
   {
     constexpr int QC = C::TILEB / 1024 / kStreams;  // copies per wave
-    char* qdst = k1 + rw * C::TILEB;
+    char* qdst = qs + rw * C::TILEB;
 #pragma unroll
     for (int i = 0; i < QC; ++i) {
       const int copy = st * QC + i;
@@ -554,7 +578,7 @@ __device__ __forceinline__ void attn_workgroup(
       __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(qdst + copy * 1024), 16, 0, 0);
     }
   }
-  // Ancestor rows of the tile's 64 query rows (row r: node (tile_row0 + r)
+  // Ancestor rows of the tile's query rows (row r: node (tile_row0 + r)
   // / G, clamped to the last row), staged in LDS when the workgroup's key
   // range reaches the tree block, after the copies above are on their way;
   // a masked block then reads its two words from LDS. Only the Wn =
@@ -577,8 +601,11 @@ __device__ __forceinline__ void attn_workgroup(
   {
     const int n_first = div_G.quot(tile_row0);
     const int n_last = div_G.quot(min(R - 1, tile_row0 + kRowsPerTile - 1));
-    const int n = n_first + lane;  // at most 64 nodes per tile
-    if (n <= n_last) own = (anc[(int64_t)n * W + (n >> 5)] >> (n & 31)) & 1u;
+#pragma unroll
+    for (int u = 0; u < kRowsPerTile / 64; ++u) {  // at most kRowsPerTile nodes
+      const int n = n_first + 64 * u + lane;
+      if (n <= n_last) own |= (anc[(int64_t)n * W + (n >> 5)] >> (n & 31)) & 1u;
+    }
   }
   const uint32_t* myrow = mrows + (rw * 32 + j) * Wn;
   auto vis_of = [&](int key0) {
@@ -608,7 +635,7 @@ __device__ __forceinline__ void attn_workgroup(
   // barrier before step 0 copies into k1.
   bf16x8 qf[C::KS];
   {
-    const char* qrow = k1 + rw * C::TILEB + j * C::ROWB;
+    const char* qrow = qs + rw * C::TILEB + j * C::ROWB;
     const int f = fk<D>(j);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
@@ -636,18 +663,18 @@ __device__ __forceinline__ void attn_workgroup(
     // resource.
     const auto rk = block_rsrc<D>(kh, (sb_at(i + 1) * kStreams + st) * kBK, KT, i + 1 < nsb);
     const auto rv = block_rsrc<D>(vh, key0, KT, true);
-    auto kcopy = [&](int c) { copy_part<D, false>(rk, kn + soff, rw, cl, c); };
-    auto vcopy = [&](int c) { copy_part<D, true>(rv, vdst + soff, rw, cl, c); };
+    auto kcopy = [&](int c) { copy_part<D, RW, false>(rk, kn + soff, rw, cl, c); };
+    auto vcopy = [&](int c) { copy_part<D, RW, true>(rv, vdst + soff, rw, cl, c); };
     __builtin_amdgcn_sched_barrier(0);
-    const f32x16 sacc = block_qk<D>(kc + soff, qf, lane, kcopy);
+    const f32x16 sacc = block_qk<D, RW>(kc + soff, qf, lane, kcopy);
     __builtin_amdgcn_sched_barrier(0);
     const bool masked = key0 + kBK > S;
     const uint32_t vis = vis_of(key0);
     if (first)
-      block_softmax_pv<D, false>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
+      block_softmax_pv<D, RW, false>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
                                  masked, vis, vcopy);
     else
-      block_softmax_pv<D, true>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
+      block_softmax_pv<D, RW, true>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
                                 masked, vis, vcopy);
     // Keep the wait for the copies at the end of the step: the scheduler
     // would otherwise hoist it (and the barrier) above the vector work.
@@ -666,27 +693,41 @@ __device__ __forceinline__ void attn_workgroup(
   block_pv<D>(((nsb - 1) & 1 ? v1 : v0) + soff, vl, pb, o, lsum);
   __syncthreads();
 
-  // Merge the four streams. Every wave parks its (reference max, sum) and
-  // the fp32 output tiles it does not merge itself in LDS; then the wave of
-  // stream s merges the 32-dim output tile dt = s of its rows over the
-  // streams, its own share straight from registers.
+  // Merge the streams. Every wave parks its (reference max, sum) and the
+  // fp32 output tiles it does not merge itself in LDS; then the wave of
+  // stream s merges the MT 32-dim output tiles [s MT, (s + 1) MT) of its
+  // rows over the streams, its own share straight from registers. Wave
+  // w = s RW + r parks in stage array w / 2 (k0, v0, k1, v1), at offset
+  // (w mod 2) PB. Four streams (MT = 1; with D = 64 streams 2 and 3 merge
+  // nothing): a wave's slot holds all DT tiles, its own unused. Two streams
+  // (MT = DT / 2): it holds only the DT - MT tiles the other stream merges,
+  // so that the eight slots fit the smaller stage arrays.
+  constexpr int MT = (C::DT + kStreams - 1) / kStreams;
+  constexpr bool kCompact = kStreams == 2;
+  constexpr int PB = (kCompact ? C::DT - MT : C::DT) * 4096;
+  static_assert(2 * PB <= C::STAGEB, "two waves' parked tiles per stage array");
+  auto park_of = [&](int s_, int r_) -> char* {
+    const int w = s_ * kRowWaves + r_;
+    char* arr = (w >> 1) == 0 ? k0 : (w >> 1) == 1 ? v0 : (w >> 1) == 2 ? k1 : v1;
+    return arr + (w & 1) * PB;
+  };
+  auto pslot = [&](int s_, int d) { return kCompact && d >= s_ * MT ? d - MT : d; };
   const float l_tot = lsum[0];
   {
-    char* mine = (st == 0 ? k0 : st == 1 ? v0 : st == 2 ? k1 : v1) + rw * C::OB;
-    float4* ob = reinterpret_cast<float4*>(mine);
+    float4* ob = reinterpret_cast<float4*>(park_of(st, rw));
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      if (dt == st) continue;
+      if (dt >= st * MT && dt < (st + 1) * MT) continue;
+      const int ps = pslot(st, dt);
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd)
-        ob[(dt * 4 + qd) * 64 + lane] =
+        ob[(ps * 4 + qd) * 64 + lane] =
             make_float4(o[dt][4 * qd], o[dt][4 * qd + 1], o[dt][4 * qd + 2], o[dt][4 * qd + 3]);
     }
     mlx[wave * 64 + lane] = make_float2(m_run, l_tot);
   }
   __syncthreads();
-  if (!live || st >= C::DT) return;
-  const int dt = st;
+  if (!live || st * MT >= C::DT) return;
   float ms[kStreams], ls[kStreams];
 #pragma unroll
   for (int s = 0; s < kStreams; ++s) {
@@ -698,67 +739,76 @@ __device__ __forceinline__ void attn_workgroup(
 #pragma unroll
   for (int s = 1; s < kStreams; ++s) M = fmaxf(M, ms[s]);
   const float Mu = M == -INFINITY ? 0.f : M;
-  float L = 0.f, acc[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  float L = 0.f, ws_[kStreams];
 #pragma unroll
   for (int s = 0; s < kStreams; ++s) {
-    const float w = __builtin_amdgcn_exp2f(ms[s] - Mu);
-    L += w * ls[s];
-    if (s == st) {
-#pragma unroll
-      for (int d = 0; d < C::DT; ++d)
-        if (d == st) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] += w * o[d][r];
-        }
-      continue;
-    }
-    const char* src = (s == 0 ? k0 : s == 1 ? v0 : s == 2 ? k1 : v1) + rw * C::OB;
-    const float4* ob = reinterpret_cast<const float4*>(src);
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const float4 x = ob[(dt * 4 + qd) * 64 + lane];
-      acc[4 * qd] += w * x.x;
-      acc[4 * qd + 1] += w * x.y;
-      acc[4 * qd + 2] += w * x.z;
-      acc[4 * qd + 3] += w * x.w;
-    }
+    ws_[s] = __builtin_amdgcn_exp2f(ms[s] - Mu);
+    L += ws_[s] * ls[s];
   }
-  if (!row_ok) return;
-  if (splits == 1) {
-    const float inv = 1.0f / L;
-    uint16_t* orow = out + ((int64_t)node * Hq + hq) * D;
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int d0 = 32 * dt + 8 * qd + 4 * h;
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16_rne(acc[4 * qd] * inv) |
-             ((uint32_t)f32_to_bf16_rne(acc[4 * qd + 1] * inv) << 16);
-      pk.y = (uint32_t)f32_to_bf16_rne(acc[4 * qd + 2] * inv) |
-             ((uint32_t)f32_to_bf16_rne(acc[4 * qd + 3] * inv) << 16);
-      *reinterpret_cast<uint2*>(orow + d0) = pk;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int dt = st * MT + mt;
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < kStreams; ++s) {
+      const float w = ws_[s];
+      if (s == st) {
+#pragma unroll
+        for (int d = 0; d < C::DT; ++d)
+          if (d == dt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] += w * o[d][r];
+          }
+        continue;
+      }
+      const float4* ob = reinterpret_cast<const float4*>(park_of(s, rw));
+      const int ps = pslot(s, dt);
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const float4 x = ob[(ps * 4 + qd) * 64 + lane];
+        acc[4 * qd] += w * x.x;
+        acc[4 * qd + 1] += w * x.y;
+        acc[4 * qd + 2] += w * x.z;
+        acc[4 * qd + 3] += w * x.w;
+      }
     }
-  } else {
-    // Partial tile wb of this split: the split's output normalised by its
-    // own sum, [DT][4][64 lanes] x 4 fp16, plus one fp32 (max, sum) pair
-    // per row. Normalised values lie within the V rows' range, so fp16
-    // keeps them to 2^-11 relative, well inside the final bf16 rounding;
-    // half the bytes of fp32 partials to write here and read back in the
-    // combine. Non-temporal stores: the partials are read once, by the
-    // combine kernel, and need not sit in L2 (whose dirty lines would
-    // otherwise be written back at the end of the kernel).
-    const int64_t wb =
-        ((int64_t)(part_base + split * Hkv + g) * tiles + tile) * kRowWaves + rw;
-    const float inv = L > 0.f ? 1.0f / L : 0.f;  // a split may see no key of a row
-    u32x2* po = reinterpret_cast<u32x2*>(part_o) + (wb * C::DT + dt) * 4 * 64;
+    if (!row_ok) continue;
+    if (splits == 1) {
+      const float inv = 1.0f / L;
+      uint16_t* orow = out + ((int64_t)node * Hq + hq) * D;
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd)
-      __builtin_nontemporal_store(
-          u32x2{pack_f16x2(acc[4 * qd] * inv, acc[4 * qd + 1] * inv),
-                pack_f16x2(acc[4 * qd + 2] * inv, acc[4 * qd + 3] * inv)},
-          po + qd * 64 + lane);
-    if (dt == 0 && h == 0) reinterpret_cast<float2*>(part_ml)[wb * 32 + j] = make_float2(M, L);
+      for (int qd = 0; qd < 4; ++qd) {
+        const int d0 = 32 * dt + 8 * qd + 4 * h;
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16_rne(acc[4 * qd] * inv) |
+               ((uint32_t)f32_to_bf16_rne(acc[4 * qd + 1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16_rne(acc[4 * qd + 2] * inv) |
+               ((uint32_t)f32_to_bf16_rne(acc[4 * qd + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + d0) = pk;
+      }
+    } else {
+      // Partial tile wb of this split: the split's output normalised by its
+      // own sum, [DT][4][64 lanes] x 4 fp16, plus one fp32 (max, sum) pair
+      // per row. Normalised values lie within the V rows' range, so fp16
+      // keeps them to 2^-11 relative, well inside the final bf16 rounding;
+      // half the bytes of fp32 partials to write here and read back in the
+      // combine. Non-temporal stores: the partials are read once, by the
+      // combine kernel, and need not sit in L2 (whose dirty lines would
+      // otherwise be written back at the end of the kernel).
+      const int64_t wb =
+          ((int64_t)(part_base + split * Hkv + g) * tiles + tile) * kRowWaves + rw;
+      const float inv = L > 0.f ? 1.0f / L : 0.f;  // a split may see no key of a row
+      u32x2* po = reinterpret_cast<u32x2*>(part_o) + (wb * C::DT + dt) * 4 * 64;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        __builtin_nontemporal_store(
+            u32x2{pack_f16x2(acc[4 * qd] * inv, acc[4 * qd + 1] * inv),
+                  pack_f16x2(acc[4 * qd + 2] * inv, acc[4 * qd + 3] * inv)},
+            po + qd * 64 + lane);
+      if (dt == 0 && h == 0) reinterpret_cast<float2*>(part_ml)[wb * 32 + j] = make_float2(M, L);
+    }
   }
 }
 
@@ -769,7 +819,7 @@ __device__ __forceinline__ int xcd_run_index(int per_xcd) {
 }
 
 // One request: its values are plain arguments.
-template <int D>
+template <int D, int RW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void tree_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int S, int S_cap, int N, int Hq, int Hkv, float scale_log2,
@@ -778,14 +828,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int sb_per_split, int wgs, int per_xcd) {
   const int idx = xcd_run_index(per_xcd);
   if (idx >= wgs) return;
-  attn_workgroup<D>(q, k, v, S, S_cap, N, Hq, Hkv, scale_log2, anc, W, out, part_o, part_ml,
-                    tiles, splits, 0, sb_per_split, idx);
+  attn_workgroup<D, RW>(q, k, v, S, S_cap, N, Hq, Hkv, scale_log2, anc, W, out, part_o,
+                        part_ml, tiles, splits, 0, sb_per_split, idx);
 }
 
 // Several requests: prefix lengths and cumulative workgroup ends per
 // request; request r's slices start r strides into q, anc, out and
 // kv_req_stride elements into k and v.
-template <int D>
+template <int D, int RW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void tree_attn_batched_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kv_req_stride, ReqInts S_of, ReqInts wg_end,
@@ -799,23 +849,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int wg0 = req ? wg_end.v[req - 1] : 0;
   const int S = S_of.v[req];
   const int64_t qo = (int64_t)req * N * Hq * D;
-  attn_workgroup<D>(q + qo, k + req * kv_req_stride, v + req * kv_req_stride, S, S_cap, N, Hq,
-                    Hkv, scale_log2, anc + (int64_t)req * N * W, W, out + qo, part_o, part_ml,
-                    tiles, req_splits(S, N, sb_per_split), wg0 / tiles, sb_per_split,
-                    idx0 - wg0);
+  attn_workgroup<D, RW>(q + qo, k + req * kv_req_stride, v + req * kv_req_stride, S, S_cap, N,
+                        Hq, Hkv, scale_log2, anc + (int64_t)req * N * W, W, out + qo, part_o,
+                        part_ml, tiles, req_splits<RW>(S, N, sb_per_split), wg0 / tiles,
+                        sb_per_split, idx0 - wg0);
 }
 
 // Merge the per-split partials. One thread per float4 of a partial tile
 // (the same slot in every split), so each load instruction of a wave reads
 // 1 KB contiguously; the splits are taken 8 at a time with every load of a
 // batch issued before any is used, merged by a running maximum.
-template <int D>
+template <int D, int RW>
 __device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
                                              const float* __restrict__ part_ml, int splits,
                                              int split_base, int N, int Hq, int Hkv, int tiles,
                                              const uint32_t* __restrict__ anc, int W,
                                              uint16_t* __restrict__ out) {
   constexpr int DT = D / 32;
+  constexpr int kRowWaves = Shape<RW>::kRowWaves;
+  constexpr int kRowsPerTile = Shape<RW>::kRowsPerTile;
   const int t = blockIdx.x * 256 + threadIdx.x;
   const int lane = t & 63, qd = (t >> 6) & 3;
   const int dt = (t >> 8) % DT;
@@ -884,34 +936,47 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ part_o,
   *reinterpret_cast<uint2*>(out + ((int64_t)node * Hq + hq) * D + d0) = pk;
 }
 
-template <int D>
+template <int D, int RW>
 __global__ __launch_bounds__(256) void tree_attn_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int N,
     int Hq, int Hkv, int tiles, const uint32_t* __restrict__ anc, int W,
     uint16_t* __restrict__ out) {
-  combine_rows<D>(part_o, part_ml, splits, 0, N, Hq, Hkv, tiles, anc, W, out);
+  combine_rows<D, RW>(part_o, part_ml, splits, 0, N, Hq, Hkv, tiles, anc, W, out);
 }
 
 // blockIdx.y is the request; one that ran as a single split wrote its
 // output directly.
-template <int D>
+template <int D, int RW>
 __global__ __launch_bounds__(256) void tree_attn_batched_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, ReqInts S_of,
     ReqInts wg_end, int sb_per_split, int N, int Hq, int Hkv, int tiles,
     const uint32_t* __restrict__ anc, int W, uint16_t* __restrict__ out) {
   const int req = blockIdx.y;
-  const int splits = req_splits(S_of.v[req], N, sb_per_split);
+  const int splits = req_splits<RW>(S_of.v[req], N, sb_per_split);
   if (splits == 1) return;
   const int split_base = req ? wg_end.v[req - 1] / (Hkv * tiles) : 0;
-  combine_rows<D>(part_o, part_ml, splits, split_base, N, Hq, Hkv, tiles,
-                  anc + (int64_t)req * N * W, W, out + (int64_t)req * N * Hq * D);
+  combine_rows<D, RW>(part_o, part_ml, splits, split_base, N, Hq, Hkv, tiles,
+                      anc + (int64_t)req * N * W, W, out + (int64_t)req * N * Hq * D);
 }
 
 // Workgroups resident at once: one per CU (LDS holds one).
 constexpr int kSlots = 256;
 
+// The tile shape of a call on the host: row waves, rows per tile, keys per
+// superblock and the modelled time of one superblock step (measured: about
+// 1.4 us for 128 keys x 64 rows; 64 keys x 128 rows, the same products
+// with half the copies, planned at 1.05 us).
+struct HostShape {
+  int rw, rows, sbk;
+  double step_us;
+};
+inline HostShape host_shape(int N, int Hq, int Hkv) {
+  if (N * (Hq / Hkv) >= kTallRows) return {4, Shape<4>::kRowsPerTile, Shape<4>::kSBK, 1.05};
+  return {2, Shape<2>::kRowsPerTile, Shape<2>::kSBK, 1.4};
+}
+
 // Superblocks of a key range of S + N keys.
-inline int n_superblocks(int S, int N) { return (S + N + kSBK - 1) / kSBK; }
+inline int n_superblocks(int S, int N, int sbk) { return (S + N + sbk - 1) / sbk; }
 
 // Most splits a request with nsb superblocks may be cut into, when each
 // split covers `per_split` workgroups: enough for four waves of workgroups
@@ -923,20 +988,23 @@ inline int split_budget(int nsb, int per_split) {
   return std::min(nsb, std::max(waves4, (nsb + 15) / 16));
 }
 
-// Launch model constants, measured on the 30B verifier shape: one
-// superblock step, a workgroup's fixed work (set-up, merge, write), the
-// partials' HBM rate (bytes per microsecond) and the combine launch.
-constexpr double kStepUs = 1.4, kWgUs = 4.0, kPartBytesPerUs = 5.0e6, kCombineUs = 3.0;
+// Launch model constants, measured on the 30B verifier shape: a
+// workgroup's fixed work (set-up, merge, write), the partials' HBM rate
+// (bytes per microsecond) and the combine launch (the step time is the
+// shape's).
+constexpr double kWgUs = 4.0, kPartBytesPerUs = 5.0e6, kCombineUs = 3.0;
 
 // Modelled time of the launch with `sbps` superblocks per split. The
 // workgroups run in id order; XCD x takes the contiguous id range the kernel
 // maps to it, and each of its CUs (slots / 8, one resident workgroup each)
 // takes the next workgroup when it frees up. A workgroup lasts its split's
-// superblocks times kStepUs plus kWgUs. Splitting adds the partials' round
-// trip through HBM and the combine launch. Returns early (with a value at
-// least `cap`) once the bound exceeds cap.
-double model_us(int nreq, const int* S, int N, int Hkv, int D, int tiles, int rows_pad, int sbps,
-                double cap) {
+// superblocks times the step time plus kWgUs. Splitting adds the partials'
+// round trip through HBM and the combine launch. Returns early (with a
+// value at least `cap`) once the bound exceeds cap.
+double model_us(int nreq, const int* S, int N, int Hkv, int D, const HostShape& sh, int tiles,
+                int rows_pad, int sbps, double cap) {
+  const int kSBK = sh.sbk;
+  const double kStepUs = sh.step_us;
   const int slots = kSlots;
   const int cus = slots / kXcds;
   int64_t splits_total = 0;
@@ -996,7 +1064,9 @@ struct PlanKey {
 // only those that cut no request into more splits than its split_budget.
 // The last choice is kept per thread, so the calls of one round (every
 // layer, same prefix lengths) plan once.
-int choose_sbps(int nreq, const int* S, int N, int Hq, int Hkv, int D, int tiles, int rows_pad) {
+int choose_sbps(int nreq, const int* S, int N, int Hq, int Hkv, int D, const HostShape& sh,
+                int tiles, int rows_pad) {
+  const int kSBK = sh.sbk;
   thread_local PlanKey last{};
   thread_local int last_sbps = 0;
   PlanKey key{};
@@ -1012,7 +1082,7 @@ int choose_sbps(int nreq, const int* S, int N, int Hq, int Hkv, int D, int tiles
   // Shortest split length that keeps every request within its budget.
   int sbps_min = 1;
   for (int r = 0; r < nreq; ++r) {
-    const int nsb = n_superblocks(S[r], N);
+    const int nsb = n_superblocks(S[r], N, kSBK);
     const int b = split_budget(nsb, Hkv * tiles);
     sbps_min = std::max(sbps_min, (nsb + b - 1) / b);
   }
@@ -1026,9 +1096,9 @@ int choose_sbps(int nreq, const int* S, int N, int Hq, int Hkv, int D, int tiles
   std::sort(cand, cand + nc, std::greater<int>());
   nc = (int)(std::unique(cand, cand + nc) - cand);
   int best = cand[0];
-  double best_us = model_us(nreq, S, N, Hkv, D, tiles, rows_pad, best, 1e300);
+  double best_us = model_us(nreq, S, N, Hkv, D, sh, tiles, rows_pad, best, 1e300);
   for (int i = 1; i < nc; ++i) {
-    const double t = model_us(nreq, S, N, Hkv, D, tiles, rows_pad, cand[i], best_us);
+    const double t = model_us(nreq, S, N, Hkv, D, sh, tiles, rows_pad, cand[i], best_us);
     if (t < best_us) {
       best_us = t;
       best = cand[i];
@@ -1067,14 +1137,17 @@ int attn_static_scratch(void** ptr) {
 AttnPlan attn_plan(int nreq, const int* S, int N, int Hq, int Hkv, int D) {
   AttnPlan p{};
   const int G = Hq / Hkv, R = N * G;
+  const HostShape sh = host_shape(N, Hq, Hkv);
+  const int kSBK = sh.sbk;
   p.nreq = nreq;
-  p.tiles = (R + kRowsPerTile - 1) / kRowsPerTile;
-  p.rows_pad = p.tiles * kRowsPerTile;
+  p.row_waves = sh.rw;
+  p.tiles = (R + sh.rows - 1) / sh.rows;
+  p.rows_pad = p.tiles * sh.rows;
   const int per_split = Hkv * p.tiles;
   // One superblock count per split for every request, so requests with
   // longer prefixes get proportionally more splits; chosen by simulating
   // the launch (choose_sbps).
-  p.sb_per_split = choose_sbps(nreq, S, N, Hq, Hkv, D, p.tiles, p.rows_pad);
+  p.sb_per_split = choose_sbps(nreq, S, N, Hq, Hkv, D, sh, p.tiles, p.rows_pad);
   int wg = 0, sp = 0;
   p.any_split = false;
   for (int r = 0; r < DDTREE_MAX_REQ; ++r) {
@@ -1115,17 +1188,47 @@ AttnPlan attn_plan(int nreq, const int* S, int N, int Hq, int Hkv, int D) {
 // are non-decreasing in every S[r].
 size_t attn_workspace_bound(int nreq, const int* S, int N, int Hq, int Hkv, int D) {
   const int G = Hq / Hkv, R = N * G;
-  const int tiles = (R + kRowsPerTile - 1) / kRowsPerTile;
+  const HostShape sh = host_shape(N, Hq, Hkv);
+  const int tiles = (R + sh.rows - 1) / sh.rows;
   size_t splits = 0;
   bool can_split = false;
   for (int r = 0; r < nreq; ++r) {
-    const int b = split_budget(n_superblocks(S[r], N), Hkv * tiles);
+    const int b = split_budget(n_superblocks(S[r], N, sh.sbk), Hkv * tiles);
     splits += (size_t)b;
     can_split = can_split || b > 1;
   }
   if (!can_split) return 0;
-  const size_t rows = splits * Hkv * (size_t)tiles * kRowsPerTile;
+  const size_t rows = splits * Hkv * (size_t)tiles * sh.rows;
   return rows * D * sizeof(uint16_t) + rows * 2 * sizeof(float);
+}
+
+// The main and combine launches of a plan with tile shape RW.
+template <int D, int RW>
+static int attn_launch_shape(const AttnPlan& p, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, int64_t kv_req_stride, int nreq, int S0,
+                             int S_cap, int N, int Hq, int Hkv, float scale_log2,
+                             const uint32_t* anc, int W, uint16_t* out, float* po, float* pml,
+                             hipStream_t stream) {
+  const dim3 grid(kXcds * p.per_xcd);
+  if (nreq == 1)
+    hipLaunchKernelGGL((tree_attn_kernel<D, RW>), grid, dim3(kThreads), 0, stream, q, k, v, S0,
+                       S_cap, N, Hq, Hkv, scale_log2, anc, W, out, po, pml, p.tiles,
+                       p.splits.v[0], p.sb_per_split, p.wgs, p.per_xcd);
+  else
+    hipLaunchKernelGGL((tree_attn_batched_kernel<D, RW>), grid, dim3(kThreads), 0, stream, q, k,
+                       v, kv_req_stride, p.S, p.wg_end, S_cap, N, Hq, Hkv, scale_log2, anc, W,
+                       out, po, pml, p.tiles, p.sb_per_split, p.wgs, p.per_xcd);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !p.any_split) return launch_status(e);
+  const int threads = Hkv * p.tiles * RW * (D / 32) * 4 * 64;
+  const dim3 cgrid((threads + 255) / 256, nreq);
+  if (nreq == 1)
+    hipLaunchKernelGGL((tree_attn_combine_kernel<D, RW>), cgrid, dim3(256), 0, stream, po, pml,
+                       p.splits.v[0], N, Hq, Hkv, p.tiles, anc, W, out);
+  else
+    hipLaunchKernelGGL((tree_attn_batched_combine_kernel<D, RW>), cgrid, dim3(256), 0, stream,
+                       po, pml, p.S, p.wg_end, p.sb_per_split, N, Hq, Hkv, p.tiles, anc, W, out);
+  return launch_status(hipGetLastError());
 }
 
 int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t kv_req_stride,
@@ -1135,48 +1238,13 @@ int attn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t
   float* po = p.any_split ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_o_off) : nullptr;
   float* pml = p.any_split ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_ml_off) : nullptr;
   const float scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid(kXcds * p.per_xcd);
-  if (nreq == 1) {
-    const int splits = p.splits.v[0];
-    if (D == 128)
-      hipLaunchKernelGGL(tree_attn_kernel<128>, grid, dim3(kThreads), 0, stream, q, k, v, S[0],
-                         S_cap, N, Hq, Hkv, scale_log2, anc, W, out, po, pml, p.tiles, splits,
-                         p.sb_per_split, p.wgs, p.per_xcd);
-    else
-      hipLaunchKernelGGL(tree_attn_kernel<64>, grid, dim3(kThreads), 0, stream, q, k, v, S[0],
-                         S_cap, N, Hq, Hkv, scale_log2, anc, W, out, po, pml, p.tiles, splits,
-                         p.sb_per_split, p.wgs, p.per_xcd);
-  } else {
-    if (D == 128)
-      hipLaunchKernelGGL(tree_attn_batched_kernel<128>, grid, dim3(kThreads), 0, stream, q, k, v,
-                         kv_req_stride, p.S, p.wg_end, S_cap, N, Hq, Hkv, scale_log2, anc, W,
-                         out, po, pml, p.tiles, p.sb_per_split, p.wgs, p.per_xcd);
-    else
-      hipLaunchKernelGGL(tree_attn_batched_kernel<64>, grid, dim3(kThreads), 0, stream, q, k, v,
-                         kv_req_stride, p.S, p.wg_end, S_cap, N, Hq, Hkv, scale_log2, anc, W,
-                         out, po, pml, p.tiles, p.sb_per_split, p.wgs, p.per_xcd);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !p.any_split) return launch_status(e);
-  const int threads = Hkv * p.tiles * kRowWaves * (D / 32) * 4 * 64;
-  const dim3 cgrid((threads + 255) / 256, nreq);
-  if (nreq == 1) {
-    if (D == 128)
-      hipLaunchKernelGGL(tree_attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, po, pml,
-                         p.splits.v[0], N, Hq, Hkv, p.tiles, anc, W, out);
-    else
-      hipLaunchKernelGGL(tree_attn_combine_kernel<64>, cgrid, dim3(256), 0, stream, po, pml,
-                         p.splits.v[0], N, Hq, Hkv, p.tiles, anc, W, out);
-  } else {
-    if (D == 128)
-      hipLaunchKernelGGL(tree_attn_batched_combine_kernel<128>, cgrid, dim3(256), 0, stream, po,
-                         pml, p.S, p.wg_end, p.sb_per_split, N, Hq, Hkv, p.tiles, anc, W, out);
-    else
-      hipLaunchKernelGGL(tree_attn_batched_combine_kernel<64>, cgrid, dim3(256), 0, stream, po,
-                         pml, p.S, p.wg_end, p.sb_per_split, N, Hq, Hkv, p.tiles, anc, W, out);
-  }
-  return launch_status(hipGetLastError());
+  auto go = [&](auto launch) {
+    return launch(p, q, k, v, kv_req_stride, nreq, S[0], S_cap, N, Hq, Hkv, scale_log2, anc, W,
+                  out, po, pml, stream);
+  };
+  if (D == 128)
+    return p.row_waves == 4 ? go(attn_launch_shape<128, 4>) : go(attn_launch_shape<128, 2>);
+  return p.row_waves == 4 ? go(attn_launch_shape<64, 4>) : go(attn_launch_shape<64, 2>);
 }
-
 
 }  // namespace ddt_host

@@ -33,8 +33,9 @@ int build_launch(const float* logp, const int32_t* token, int L, int K, int B, i
 // requests of N nodes each with their own prefix lengths.
 struct AttnPlan {
   int nreq;
-  int tiles, rows_pad;    // 64-row query tiles per kv-head
-  int sb_per_split;       // 128-key superblocks per split, every request
+  int row_waves;          // tile shape: 2 (64-row tiles, 128-key superblocks) or 4 (128, 64)
+  int tiles, rows_pad;    // query tiles per kv-head, and their rows
+  int sb_per_split;       // superblocks per split, every request
   ReqInts S, splits;      // per request: prefix length, splits of its key range
   ReqInts wg_end;         // per request: end of its workgroup range
   ReqInts split_base;     // per request: its first split in the partials

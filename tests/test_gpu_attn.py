@@ -230,3 +230,46 @@ def test_large_values_through_split_partials():
     ref = oa.tree_attention(q, kv[0], kv[1], S, anc, 0.25)
     assert np.abs(ref).max() > 1000.0  # the outputs do reach the large scale
     assert_attn_close(got / big, ref / big, "large V through the split path")
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,D,S,kind", [
+    (127, 32, 4, 128, 1000, "random"),  # 1016 rows per kv-head: 64-row tiles
+    (128, 32, 4, 128, 1000, "random"),  # 1024 rows: 128-row tiles from here on
+    (129, 32, 4, 128, 1000, "random"),  # 1032 rows: a last tile of 8 rows
+    (129, 8, 1, 64, 0, "random"),       # D = 64, no prefix
+    (300, 16, 4, 128, 2500, "chain"),   # several splits
+    (1025, 4, 4, 128, 300, "random"),   # G = 1: 128 nodes per tile
+    (1025, 8, 4, 64, 77, "star"),
+])
+def test_tall_tiles_every_element(N, Hq, Hkv, D, S, kind):
+    """Both tile shapes around the switch at 1024 query rows per kv-head
+    (N * G): every output element against the oracle, and a second call
+    bit-identical to the first."""
+    q_bits, q, kv_bits, kv, g = _inputs(N, Hq, Hkv, D, S, 40 + N + S + D)
+    anc = _tree_anc(kind, N, g)
+    _run(q_bits, q, kv_bits, kv, S, anc, twice=True)
+
+
+@pytest.mark.parametrize("S", [200, 3000])
+def test_pruned_rows_in_tall_tiles(S):
+    """A star of 1025 nodes at G = 1 (128 nodes per tile) with rows of
+    dropped leaves emptied as ddtree_tree_prune leaves them: a whole tile
+    dropped (nodes 256-383), a tile whose first 64 nodes are dropped and
+    last 64 kept (640-703), one whose last 64 are dropped (960-1023), and
+    scattered single nodes. A tile with any kept node must run: the kept
+    rows are compared with the oracle (the dropped rows are unspecified)."""
+    N, Hq, Hkv, D = 1025, 2, 2, 128
+    q_bits, q, kv_bits, kv, g = _inputs(N, Hq, Hkv, D, S, 60 + S)
+    anc = _tree_anc("star", N, g)
+    dropped = set(range(256, 384)) | set(range(640, 704)) | set(range(960, 1024)) | {5, 130, 517}
+    anc = anc.copy()
+    for n in dropped:
+        anc[n] = 0
+    kept = [n for n in range(N) if n not in dropped]
+    say(f"attn pruned tall tiles S={S} kept={len(kept)}")
+    qd = up_bf16(q_bits)
+    kvd = up_bf16(kv_bits)
+    out = bd.ddtree_tree_attn(qd, kvd[0], kvd[1], S, up(anc.view(np.int32)))
+    got = down_bf16_f32(out)[kept]
+    ref = oa.tree_attention(q, kv[0], kv[1], S, anc, nodes=kept)[kept]
+    assert_attn_close(got, ref, f"pruned star N={N} S={S}")
