@@ -141,6 +141,8 @@ def _attn_batch(R, N, Hq, Hkv, D, S, seed, layers=2, layer=1):
     (3, 17, 8, 2, 128, [0, 1000, 37]),
     (5, 33, 4, 1, 64, [64, 0, 513, 5, 200]),
     (2, 65, 16, 4, 128, [700, 129]),
+    (3, 129, 32, 4, 128, [0, 700, 2000]),  # 1032 rows per kv-head: 128-row tiles
+    (2, 257, 8, 2, 64, [300, 5]),          # 1028 rows, D = 64
 ])
 def test_attn_batched_small(R, N, Hq, Hkv, D, S):
     q_bits, q, kv_bits, kv, anc, got, _ = _attn_batch(R, N, Hq, Hkv, D, S, R + N)

@@ -42,3 +42,10 @@ def test_noalloc_matches_workspace_entry_two_calls():
     assert _check(65, 32, 4, 128, 4096, 1) > 0
     assert _check(33, 8, 2, 64, 700, 2) > 0
     assert _check(9, 4, 2, 64, 20, 3) == 0
+
+
+def test_noalloc_tall_tiles():
+    # 1032 query rows per kv-head (128-row tiles), then the 30B shape again
+    # (64-row tiles) in the same scratch array.
+    assert _check(129, 32, 4, 128, 2000, 4) > 0
+    assert _check(65, 32, 4, 128, 4096, 5) > 0
