@@ -59,9 +59,10 @@ def test_workspace_queries(lib):
 
 # Head layouts of the workloads (N, Hq, Hkv, D): tiny; the 8B shape and the
 # budget sweep at B = 64 and 512; the 30B shape at B = 64 and 256 (also the
-# long-context shape).
+# long-context shape); then two layouts at and past the switch to 128-row
+# tiles (1024 query rows per kv-head; 1025 nodes at G = 1).
 WORKLOAD_LAYOUTS = [(17, 4, 2, 64), (65, 32, 8, 128), (513, 32, 8, 128), (65, 32, 4, 128),
-                    (257, 32, 4, 128)]
+                    (257, 32, 4, 128), (128, 32, 4, 128), (1025, 8, 8, 64)]
 
 
 @pytest.mark.parametrize("layout", WORKLOAD_LAYOUTS)
