@@ -54,6 +54,35 @@ def test_attention_shapes(case):
 
 
 @pytest.mark.parametrize("case", range(16))
+def test_tall_attention_shapes(case):
+    """Shapes with at least 1024 query rows per kv-head (128-row tiles):
+    node counts from 128 to 1025, group sizes 1-8, both head sizes, prefixes
+    from empty to several splits, random tree shapes; sampled (node, head)
+    rows, the first and last node included."""
+    g = synth.rng("test", 803, case)
+    D = int(g.choice([64, 128]))
+    Hkv = int(g.choice([1, 2, 4]))
+    G = int(g.choice([1, 2, 4, 8]))
+    Hq = Hkv * G
+    N = int(g.integers(-(-1024 // G), 1026))
+    S = int(g.choice([0, 1, 100, 777, 3000]))
+    S_cap = S + N + int(g.integers(0, 40))
+    W = (N + 31) // 32 + int(g.integers(0, 2))
+    scale = float(g.uniform(0.05, 0.2))
+    say(f"sweep tall attn case={case} N={N} Hq={Hq} Hkv={Hkv} D={D} S={S} S_cap={S_cap} W={W}")
+    q_bits, q = synth.normal_bf16(g, (N, Hq, D))
+    kv_bits, kv = synth.normal_bf16(g, (2, Hkv, S_cap, D))
+    anc = ot.ancestor_mask(_random_parent(g, N), W)
+    out = bd.ddtree_tree_attn(up_bf16(q_bits), up_bf16(kv_bits[0]), up_bf16(kv_bits[1]), S,
+                              up(anc.view(np.int32)), scale)
+    nodes = sorted({0, N - 1} | set(g.choice(N, size=min(N, 24), replace=False).tolist()))
+    heads = sorted({0, Hq - 1} | set(g.choice(Hq, size=min(Hq, 3), replace=False).tolist()))
+    ref = oa.tree_attention(q, kv[0], kv[1], S, anc, scale, nodes=nodes, heads=heads)
+    got = down_bf16_f32(out)
+    assert_attn_close(got[np.ix_(nodes, heads)], ref[np.ix_(nodes, heads)], f"tall case {case}")
+
+
+@pytest.mark.parametrize("case", range(16))
 def test_batched_attention_shapes(case):
     g = synth.rng("test", 801, case)
     R = int(g.integers(2, 7))
