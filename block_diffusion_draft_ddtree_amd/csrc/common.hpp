@@ -62,10 +62,12 @@ constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i within 8 lanes
 constexpr int kDppRowMirror = 0x140;      // lane i <-> 15 - i within 16 lanes
 
+// Every pattern above reads a lane of the same row, so each lane gets a
+// value: a plain DPP move (bound_ctrl), which needs no copy of an old value
+// and can fuse into the consuming instruction.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
-                                                    0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 struct OpMax {
