@@ -38,6 +38,7 @@ constexpr int kSurvCap = 16384;                      // survivors selected in LD
 constexpr int kLoadBatchSmall = 8;                   // candidates loaded per thread at once:
 constexpr int kLoadBatchLarge = 16;                  // the small batch when it holds all
 constexpr int kRankAllMax = 256;                     // survivors ranked all against all
+constexpr int kFusedHistK = 64;                      // larger K count digits while gathering
 constexpr int kBounds = 7;                           // per-chunk bounds: r = 1, 2, 4, ..., 64
 constexpr int kMaxCap = DDTREE_MAX_K + kLooseExtra;  // candidate slots per chunk
 
@@ -741,26 +742,46 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     }
   };
 
-  // Survivors: the candidates >= tau (every top-K element is one), each also
-  // counted in the histogram of the first digit relative to the row max
-  // (used when there are too many to rank all against all).
+  // Survivors: the candidates >= tau (every top-K element is one). They
+  // are counted in the histogram of the first digit relative to the row
+  // max, used when there are too many to rank all against all: for
+  // K > kFusedHistK as they are gathered (there are usually too many), for
+  // smaller K only then, from the survivors in LDS (or, when they overflowed
+  // it, by a counting pass over the candidates).
   auto gather = [&](uint32_t* counter, auto keep) {
     if (per_thread <= kLoadBatchSmall)
       gather_nb(std::integral_constant<int, kLoadBatchSmall>{}, counter, keep);
     else
       gather_nb(std::integral_constant<int, kLoadBatchLarge>{}, counter, keep);
   };
-  gather(&s.nsurv, [&](float x) {
-    const bool k = x >= tau;
-    if (k) atomicAdd(&s.sh.hist[0][rel_digit(M, x)], 1u);
-    return k;
-  });
+  const bool fused_hist = K > kFusedHistK;
+  if (fused_hist) {
+    gather(&s.nsurv, [&](float x) {
+      const bool k = x >= tau;
+      if (k) atomicAdd(&s.sh.hist[0][rel_digit(M, x)], 1u);
+      return k;
+    });
+  } else {
+    gather(&s.nsurv, [&](float x) { return x >= tau; });
+  }
   lds_barrier();
   int nsurv = (int)s.nsurv;
   if (nsurv <= kRankAllMax) {
     // Few survivors: rank each among all of them.
     rank_and_write(s.sx, s.si, s.rk, s.rkc, nsurv, K, lse, out_lp, out_tok);
     return;
+  }
+  if (!fused_hist) {
+    if (nsurv <= kSurvCap) {
+      for (int i = t; i < nsurv; i += kMergeThreads)
+        atomicAdd(&s.sh.hist[0][rel_digit(M, s.sx[i])], 1u);
+    } else {
+      gather(&s.nkeep, [&](float x) {  // counts only (appends nothing)
+        if (x >= tau) atomicAdd(&s.sh.hist[0][rel_digit(M, x)], 1u);
+        return false;
+      });
+    }
+    lds_barrier();
   }
 
   // The bucket d0 of the row's K-th largest: survivors in it or above it
