@@ -68,16 +68,18 @@ def test_ties_beyond_lds():
 
 
 def test_many_survivors_small_k():
-    """K <= 128 with more survivors than the merge ranks all against all:
-    a tie-heavy row at K = 64 (survivors in LDS), and 64 chunks of 4096
-    that each hold 300 values tied at the row maximum at K = 128 (19200
-    survivors: more than the merge keeps in LDS)."""
+    """K <= 64 (the merge counts the digit histogram only on demand) with
+    more survivors than it ranks all against all: a tie-heavy row (the
+    survivors fit LDS), and 64 chunks of 4096 that each hold 300 values tied
+    at the row maximum (19200 survivors, more than LDS holds: a counting
+    pass over the candidates); also K = 128 on the latter."""
     g = synth.rng("test", 505, 0)
     _check(synth.tie_logits(2, 20000, g, levels=3), 64)
     V = 64 * 4096
     x = (-1.0 - g.random((2, V))).astype(np.float32)
     for c in range(64):
         x[:, c * 4096 + g.choice(4096, 300, replace=False)] = 3.0
+    _check(x, 64)
     _check(x, 128)
 
 
