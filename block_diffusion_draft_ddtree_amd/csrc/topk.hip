@@ -679,8 +679,8 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   // Chunk c's list is read by the tpc = floor(1024 / C) threads
   // [c tpc, (c + 1) tpc), thread u of them taking positions u, u + tpc,
   // u + 2 tpc, ...: a thread reads its chunk's count once and then issues
-  // all its loads (one pass of NB per thread; one pass at K = 64 on the
-  // full vocabulary, 38 chunks x <= 137) before using any. NB is 8 when
+  // a pass of up to NB loads before using any (one pass at K = 64 on the
+  // full vocabulary, 38 chunks x <= 137 candidates). NB is 8 when
   // that covers the longest list, else 16 (measured: the 16-wide form is
   // slower at small K although its extra iterations are skipped by uniform
   // branches, and faster at large K, where it saves passes). A thread's kept
