@@ -656,15 +656,28 @@ __device__ __forceinline__ void attn_workgroup(
   auto step = [&](int i, bool first, const char* kc, char* kn, char* vdst, const char* vprev) {
     const int key0 = (sb_at(i) * kStreams + st) * kBK;
     // The copies enter the texture-address unit at about 45 B per clock per
-    // CU, and a wave whose copies are queued there cannot issue further; so
-    // they are spread over the step one at a time between products: K of
-    // the next superblock (none after the last) in the score products, V
-    // in the P.V products. Branch-free: a block not wanted has an empty
-    // resource.
+    // CU, and a wave whose copies are queued there cannot issue further.
+    // With 64-row tiles (8 copies per wave and step) they are spread over
+    // the step one at a time between products: K of the next superblock
+    // (none after the last) in the score products, V in the P.V products.
+    // With 128-row tiles (4 per wave) all go out at the start of the step,
+    // so that the last ones are not still on their way from L2 when the
+    // step ends. Branch-free: a block not wanted has an empty resource.
+    constexpr bool kEarlyCopies = RW == 4;
     const auto rk = block_rsrc<D>(kh, (sb_at(i + 1) * kStreams + st) * kBK, KT, i + 1 < nsb);
     const auto rv = block_rsrc<D>(vh, key0, KT, true);
-    auto kcopy = [&](int c) { copy_part<D, RW, false>(rk, kn + soff, rw, cl, c); };
-    auto vcopy = [&](int c) { copy_part<D, RW, true>(rv, vdst + soff, rw, cl, c); };
+    if constexpr (kEarlyCopies) {
+#pragma unroll
+      for (int c = 0; c < C::COPIES; ++c) copy_part<D, RW, false>(rk, kn + soff, rw, cl, c);
+#pragma unroll
+      for (int c = 0; c < C::COPIES; ++c) copy_part<D, RW, true>(rv, vdst + soff, rw, cl, c);
+    }
+    auto kcopy = [&](int c) {
+      if constexpr (!kEarlyCopies) copy_part<D, RW, false>(rk, kn + soff, rw, cl, c);
+    };
+    auto vcopy = [&](int c) {
+      if constexpr (!kEarlyCopies) copy_part<D, RW, true>(rv, vdst + soff, rw, cl, c);
+    };
     __builtin_amdgcn_sched_barrier(0);
     const f32x16 sacc = block_qk<D, RW>(kc + soff, qf, lane, kcopy);
     __builtin_amdgcn_sched_barrier(0);
