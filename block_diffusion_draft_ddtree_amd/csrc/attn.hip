@@ -385,16 +385,14 @@ __device__ __forceinline__ f32x16 block_qk(const char* Kb, const bf16x8 (&qf)[Cf
 // the previous block's products are added, so it also scales that block's
 // pending weights (they were formed against the old reference maximum).
 // For blocks reaching past S, `vis` (block_visibility) masks the scores by
-// a wave-uniform branch that touches only the scores. The copies
-// vcopy(0 .. COPIES - 1) (this block's V, into the stage the next step
-// reads) go between the products when PV, else after the score reduction.
-template <int D, int RW, bool PV, class VCopy>
+// a wave-uniform branch that touches only the scores.
+template <int D, bool PV>
 __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
                                                  const VLanes<D>& vl, PBlock& pb,
                                                  f32x16 (&o)[Cfg<D>::DT], float& m_run,
                                                  f32x16& lsum, float c, int lane, bool masked,
-                                                 uint32_t vis, VCopy vcopy) {
-  using C = Cfg<D, RW>;
+                                                 uint32_t vis) {
+  using C = Cfg<D>;
   const int h = lane >> 5;
   bf16x8 va[2][C::DT];
   if (PV) read_v<D>(Vprev, vl, va);
@@ -429,11 +427,6 @@ __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
     }
     m_run = m_new;
   }
-  if (!PV) {
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < C::COPIES; ++i) vcopy(i);
-  }
   __builtin_amdgcn_sched_barrier(0);
   if (PV) {
     const bf16x8 ones = bf16_ones();
@@ -452,16 +445,11 @@ __device__ __forceinline__ void block_softmax_pv(f32x16 sacc, const char* Vprev,
   for (int r = 0; r < 16; ++r)
     pb.p[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[r], c, neg_m));
   if (PV) {
-#pragma unroll
-    for (int i = 0; i < C::COPIES; ++i) vcopy(i);
-    // Interleave: one product, then a slice of the vector work, and every
-    // other product a copy.
-    static_assert(2 * C::COPIES <= 2 * C::DT + 2, "a copy every other product");
+    // Interleave: one product, then a slice of the vector work.
 #pragma unroll
     for (int i = 0; i < 2 * C::DT + 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
-      if ((i & 1) && (i >> 1) < C::COPIES) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
     }
   }
 }
@@ -656,27 +644,24 @@ __device__ __forceinline__ void attn_workgroup(
   auto step = [&](int i, bool first, const char* kc, char* kn, char* vdst, const char* vprev) {
     const int key0 = (sb_at(i) * kStreams + st) * kBK;
     // The copies enter the texture-address unit at about 45 B per clock per
-    // CU, and a wave whose copies are queued there cannot issue further.
-    // With 64-row tiles (8 copies per wave and step) they are spread over
-    // the step one at a time between products: K of the next superblock
-    // (none after the last) in the score products, V in the P.V products.
-    // With 128-row tiles (4 per wave) all go out at the start of the step,
-    // so that the last ones are not still on their way from L2 when the
-    // step ends. Branch-free: a block not wanted has an empty resource.
-    constexpr bool kEarlyCopies = RW == 4;
+    // CU, and a wave whose copies are queued there cannot issue further;
+    // but a copy issued late in the step is still on its way from L2 when
+    // the step ends. V of this superblock goes out at the start of the
+    // step; K of the next one (none after the last) too with 128-row tiles
+    // (4 copies per wave and step in all), and one at a time between the
+    // score products with 64-row tiles (8 per wave and step). Branch-free:
+    // a block not wanted has an empty resource.
+    constexpr bool kEarlyK = RW == 4;
     const auto rk = block_rsrc<D>(kh, (sb_at(i + 1) * kStreams + st) * kBK, KT, i + 1 < nsb);
     const auto rv = block_rsrc<D>(vh, key0, KT, true);
-    if constexpr (kEarlyCopies) {
+    if constexpr (kEarlyK) {
 #pragma unroll
       for (int c = 0; c < C::COPIES; ++c) copy_part<D, RW, false>(rk, kn + soff, rw, cl, c);
-#pragma unroll
-      for (int c = 0; c < C::COPIES; ++c) copy_part<D, RW, true>(rv, vdst + soff, rw, cl, c);
     }
+#pragma unroll
+    for (int c = 0; c < C::COPIES; ++c) copy_part<D, RW, true>(rv, vdst + soff, rw, cl, c);
     auto kcopy = [&](int c) {
-      if constexpr (!kEarlyCopies) copy_part<D, RW, false>(rk, kn + soff, rw, cl, c);
-    };
-    auto vcopy = [&](int c) {
-      if constexpr (!kEarlyCopies) copy_part<D, RW, true>(rv, vdst + soff, rw, cl, c);
+      if constexpr (!kEarlyK) copy_part<D, RW, false>(rk, kn + soff, rw, cl, c);
     };
     __builtin_amdgcn_sched_barrier(0);
     const f32x16 sacc = block_qk<D, RW>(kc + soff, qf, lane, kcopy);
@@ -684,11 +669,11 @@ __device__ __forceinline__ void attn_workgroup(
     const bool masked = key0 + kBK > S;
     const uint32_t vis = vis_of(key0);
     if (first)
-      block_softmax_pv<D, RW, false>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
-                                 masked, vis, vcopy);
+      block_softmax_pv<D, false>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
+                                 masked, vis);
     else
-      block_softmax_pv<D, RW, true>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
-                                masked, vis, vcopy);
+      block_softmax_pv<D, true>(sacc, vprev + soff, vl, pb, o, m_run, lsum, scale_log2, lane,
+                                masked, vis);
     // Keep the wait for the copies at the end of the step: the scheduler
     // would otherwise hoist it (and the barrier) above the vector work.
     __builtin_amdgcn_sched_barrier(0);
