@@ -646,23 +646,15 @@ __device__ __forceinline__ void attn_workgroup(
     // The copies enter the texture-address unit at about 45 B per clock per
     // CU, and a wave whose copies are queued there cannot issue further;
     // but a copy issued late in the step is still on its way from L2 when
-    // the step ends. V of this superblock goes out at the start of the
-    // step; K of the next one (none after the last) too with 128-row tiles
-    // (4 copies per wave and step in all), and one at a time between the
-    // score products with 64-row tiles (8 per wave and step). Branch-free:
-    // a block not wanted has an empty resource.
-    constexpr bool kEarlyK = RW == 4;
+    // the step ends. So V of this superblock goes out at the start of the
+    // step, and K of the next one (none after the last) one copy at a time
+    // between the last score products. Branch-free: a block not wanted has
+    // an empty resource.
     const auto rk = block_rsrc<D>(kh, (sb_at(i + 1) * kStreams + st) * kBK, KT, i + 1 < nsb);
     const auto rv = block_rsrc<D>(vh, key0, KT, true);
-    if constexpr (kEarlyK) {
-#pragma unroll
-      for (int c = 0; c < C::COPIES; ++c) copy_part<D, RW, false>(rk, kn + soff, rw, cl, c);
-    }
 #pragma unroll
     for (int c = 0; c < C::COPIES; ++c) copy_part<D, RW, true>(rv, vdst + soff, rw, cl, c);
-    auto kcopy = [&](int c) {
-      if constexpr (!kEarlyK) copy_part<D, RW, false>(rk, kn + soff, rw, cl, c);
-    };
+    auto kcopy = [&](int c) { copy_part<D, RW, false>(rk, kn + soff, rw, cl, c); };
     __builtin_amdgcn_sched_barrier(0);
     const f32x16 sacc = block_qk<D, RW>(kc + soff, qf, lane, kcopy);
     __builtin_amdgcn_sched_barrier(0);
