@@ -741,6 +741,24 @@ def oracle_round(w, lg, tgt_np, layers: int) -> dict:
     return t
 
 
+def oracle_build_forms(w, lg) -> dict:
+    """Seconds the oracle's two exact top-B constructions take on the round's
+    log-prob table: the sort-and-expand fixed point (the build the round
+    uses) and Proposition 3 as a textbook binary-heap best-first search."""
+    from oracle import softmax_topk as st
+    from oracle import tree as ot
+
+    lp, _ = st.topk(lg.x, w.K)
+    lp32 = lp.astype(np.float32)
+    out = {}
+    for name, fn in (("sort_fixed_point", ot.top_b_sort_expand),
+                     ("best_first_heap", ot.top_b_best_first)):
+        t0 = time.perf_counter()
+        fn(lp32, w.B)
+        out[name] = round(time.perf_counter() - t0, 5)
+    return out
+
+
 def cpu_baseline(w, lg, depth, tgt_np):
     """The CPU oracle on one whole round of the headline workload (all 48
     layers, not scaled) with numpy's BLAS at its default thread count
@@ -757,6 +775,7 @@ def cpu_baseline(w, lg, depth, tgt_np):
         t1 = oracle_round(w, lg, tgt_np, sample_layers)
     scale = w.layers / sample_layers
     us1 = 1e6 * (t1["topk"] + t1["build"] + t1["walk"] + scale * (t1["attn"] + t1["compact"]))
+    builds = oracle_build_forms(w, lg)
     return {"value": round(us, 1), "unit": "us/step", "cores": info["blas_threads"],
             "kind": "oracle",
             "sample": (f"one whole round of {w.name}: top-K over all {w.L} rows, tree build, "
@@ -770,6 +789,7 @@ def cpu_baseline(w, lg, depth, tgt_np):
                                          f"and their compaction, those two scaled by "
                                          f"{scale:g}"),
                               "stage_s": {k: round(v, 4) for k, v in t1.items()}},
+            "build_forms_s": builds,
             "host": info}
 
 
