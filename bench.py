@@ -262,6 +262,15 @@ def main():
     # ---- timed region -------------------------------------------------------
     gpu_us, wall_us, attn_us = timed_steps(run_step)
     eager_us = gpu_us if graphs is None else timed_steps(step)[0]
+    # The same round followed by the 4-byte accepted-count readback a host
+    # decode loop would make after it (a device-to-host copy and its wait):
+    # host wall time per round.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step()
+        int(rnd.n_acc.cpu()[0])
+    readback_us = (time.perf_counter() - t0) * 1e6 / args.steps
 
     # ---- per-stage device time (HIP events on the launch stream) ----------
     R = args.stage_reps
@@ -380,6 +389,7 @@ def main():
         "tree_attn_hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "tree_attn_mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4),
         "round_wall_us": round(wall_us, 2),
+        "round_with_readback_us": round(readback_us, 2),
         "stage_us": {k: round(v, 3) for k, v in stage.items()},
         "topk_TBps": round(topk_bytes(w) / (stage["topk"] * 1e-6) / 1e12, 3),
         "target_argmax_TBps": round(argmax_bytes(w) / (stage["target_argmax"] * 1e-6) / 1e12, 3),
