@@ -260,8 +260,25 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region -------------------------------------------------------
-    gpu_us, wall_us, attn_us = timed_steps(run_step)
-    eager_us = gpu_us if graphs is None else timed_steps(step)[0]
+    # The round as it runs (no events between its parts): `value`. Then the
+    # same steps with events around the attention calls of every step, which
+    # time the attention live; those events cost the round a few
+    # microseconds of pipeline gaps, so that pass's total is reported apart.
+    def plain_steps(run):
+        e0, e1 = ev(), ev()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return e0.elapsed_time(e1) * 1e3 / args.steps, (t1 - t0) * 1e6 / args.steps
+
+    gpu_us, wall_us = plain_steps(run_step)
+    instr_us, _, attn_us = timed_steps(run_step)
+    eager_us = gpu_us if graphs is None else plain_steps(step)[0]
     # The same round followed by the 4-byte accepted-count readback a host
     # decode loop would make after it (a device-to-host copy and its wait):
     # host wall time per round.
@@ -389,6 +406,7 @@ def main():
         "tree_attn_hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "tree_attn_mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4),
         "round_wall_us": round(wall_us, 2),
+        "round_with_attn_events_us": round(instr_us, 2),
         "round_with_readback_us": round(readback_us, 2),
         "stage_us": {k: round(v, 3) for k, v in stage.items()},
         "topk_TBps": round(topk_bytes(w) / (stage["topk"] * 1e-6) / 1e12, 3),
