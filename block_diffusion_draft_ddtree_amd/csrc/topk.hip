@@ -436,8 +436,10 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(
   }
   // Too many values at or above T (heavy ties or a flat chunk): select by
   // radix instead, starting with the first digit's histogram.
-  // Everyone has read out_count, and the stores above (slots the select
-  // below rewrites, possibly from another wave) have completed.
+  // Everyone has read out_count; and a full workgroup barrier (release and
+  // acquire at workgroup scope) orders the stores above before the
+  // select's stores below, which may rewrite the same slots from another
+  // wave.
   __syncthreads();
   if (t == 0) sh.out_count = 0u;
 #pragma unroll
