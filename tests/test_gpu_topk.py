@@ -146,3 +146,31 @@ def test_bounds_top_values_bunched(K):
         pos = pos[pos < base + n]
         x[1, pos] = 10.0 + g.standard_normal(pos.size).astype(np.float32)
     _check(x, K)
+
+
+def _sweep_case(i: int):
+    """Seeded shape and value mix for case i: L in 1..20, V log-uniform in
+    1..160000, K log-uniform in 1..min(V, 1024), a padded row stride in a
+    third of the cases; values normal at scale 0.5..4, with boosted peaks,
+    rounded to integers (heavy ties) or uniform."""
+    g = synth.rng("test", 600, i)
+    L = int(g.integers(1, 21))
+    V = int(np.exp(g.uniform(0, np.log(160000))))
+    K = max(1, min(V, 1024, int(np.exp(g.uniform(0, np.log(1025))))))
+    kind = i % 4
+    x = g.standard_normal((L, V)) * g.uniform(0.5, 4.0)
+    if kind == 1:
+        for r in range(L):
+            x[r, g.integers(0, V, size=min(V, 3))] += g.uniform(5, 12)
+    elif kind == 2:
+        x = np.round(x)
+    elif kind == 3:
+        x = g.uniform(-3, 3, (L, V))
+    stride = V + int(g.integers(1, 300)) if i % 3 == 0 else None
+    return x.astype(np.float32), K, stride
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_seeded_shape_sweep(i):
+    x, K, stride = _sweep_case(i)
+    _check(x, K, stride=stride, twice=False)
