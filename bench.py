@@ -145,6 +145,22 @@ def compact_bytes(w, a: int):
     return 8 * a * w.layers * w.Hkv * w.D
 
 
+def stage_roofline(w, stage: dict, a: int) -> dict:
+    """HBM-roofline fractions of the streaming stages from their stage
+    times (algorithmic bytes / time against the 8 TB/s peak), and the floor
+    each would have at that peak; build, walk and budget selection are
+    serial latency (no roofline)."""
+    out = {}
+    for name, nbytes in (("topk", topk_bytes(w)), ("target_argmax", argmax_bytes(w)),
+                         ("kv_compact", compact_bytes(w, a))):
+        us = stage[name]
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"bound": "hbm", "us": round(us, 3), "algorithmic_bytes": int(nbytes),
+                     "achieved_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "floor_us": round(nbytes / (HBM_PEAK_GBS * 1e3), 3)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -417,6 +433,7 @@ def main():
         "accepted": a_acc,
         "depth_hist": np.bincount(depth).tolist(),
         "roofline": roof,
+        "stage_roofline": stage_roofline(w, stage, a_acc),
     }
     if budget_round is not None:
         result["budget_round"] = budget_round
