@@ -149,3 +149,31 @@ def test_table_at_the_lds_limit():
     assert ref.depth.max() >= 8
     lp, tok = synth.sorted_logp_table(32, 1024, 200000, g, scale=3.0)
     _compare(lp, tok, 192)
+
+
+def _sweep_case(i: int):
+    """Seeded table shape for case i: L in 1..32, K log-uniform in 1..128 with
+    L K <= 32768, B log-uniform in 1..min(1024, prefixes); half the cases
+    with heavy ties, the others normal at scale 0.05..3."""
+    g = synth.rng("test", 610, i)
+    L = int(g.integers(1, 33))
+    K = max(1, min(128, 32768 // L, int(np.exp(g.uniform(0, np.log(129))))))
+    total = ot.num_prefixes(L, K)
+    B = max(1, min(1024, total, int(np.exp(g.uniform(0, np.log(1025))))))
+    lp, tok = synth.sorted_logp_table(L, K, 151936, g, scale=float(g.uniform(0.05, 3.0)),
+                                      ties=bool(i % 2))
+    return lp, tok, B
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_seeded_shape_sweep(i):
+    """Against Proposition 3's best-first search (pinned against brute force
+    in the oracle's tests), whose pop order is the sorted order of the set."""
+    lp, tok, B = _sweep_case(i)
+    parent, depth, ntok, score, anc = _gpu_tree(lp, tok, B)
+    ref = ot.tree_from_prefixes(ot.top_b_best_first(lp, B), lp, tok, ROOT_TOKEN)
+    np.testing.assert_array_equal(parent, ref.parent)
+    np.testing.assert_array_equal(depth, ref.depth)
+    np.testing.assert_array_equal(ntok, ref.token)
+    np.testing.assert_array_equal(score.view(np.uint32), ref.score.view(np.uint32))
+    np.testing.assert_array_equal(anc.view(np.uint32), ref.anc)
